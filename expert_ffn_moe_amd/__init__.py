@@ -1,0 +1,290 @@
+"""Python binding of libmoe, the MI355X (gfx950) MoE-layer hot path.
+
+Argument marshalling only: every function checks shapes/dtypes/devices of torch tensors,
+allocates outputs with torch (device memory and streams are all torch is used for) and
+calls the C ABI declared in include/moe.h on torch's current HIP stream.  All compute runs
+in the library's HIP kernels; if libmoe.so is missing or fails to load, importing this
+package raises -- there is no other implementation.
+
+Call names follow the C ABI: route, dispatch, expert_gate_up, expert_down, expert_ffn,
+combine, layer, plus pack_weights for the one-time weight packing.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16 = 0, 1
+OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER = range(5)
+W_GATE_UP, W_DOWN = 0, 1
+
+EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_packed_bytes",
+           "moe_pack_weights", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+           "moe_expert_down", "moe_combine", "moe_layer")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+class MoeProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("T", "H", "E", "k", "I", "capacity", "renormalize", "act_dtype", "w_dtype")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python expert_ffn_moe_amd/build.py` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    PP = ctypes.POINTER(MoeProblem)
+    sz = ctypes.c_size_t
+    sigs = {
+        "moe_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "moe_problem_check": (ctypes.c_int, [PP]),
+        "moe_workspace_bytes": (sz, [PP, ctypes.c_int]),
+        "moe_packed_bytes": (sz, [PP, ctypes.c_int]),
+        "moe_pack_weights": (ctypes.c_int, [PP, P, P, P, P, P, P]),
+        "moe_route": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
+        "moe_dispatch": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, sz, P]),
+        "moe_expert_ffn": (ctypes.c_int, [PP, P, P, P, P, P, P, sz, P]),
+        "moe_expert_gate_up": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
+        "moe_expert_down": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
+        "moe_combine": (ctypes.c_int, [PP, P, P, P, P, P]),
+        "moe_layer": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_str(status: int) -> str:
+    return lib.moe_status_str(int(status)).decode()
+
+
+@dataclasses.dataclass(frozen=True)
+class Problem:
+    """Shapes of one layer call (see moe_problem in include/moe.h)."""
+    T: int
+    H: int
+    E: int
+    k: int
+    I: int
+    capacity: int = 0
+    renormalize: int = 1
+    dtype: str = "bf16"  # activations and weights: "bf16" or "f32"
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def c(self) -> MoeProblem:
+        dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
+        return MoeProblem(self.T, self.H, self.E, self.k, self.I, self.capacity, self.renormalize,
+                          dt, dt)
+
+    def check(self) -> int:
+        c = self.c()
+        return lib.moe_problem_check(ctypes.byref(c))
+
+    def workspace_bytes(self, op: int) -> int:
+        c = self.c()
+        return int(lib.moe_workspace_bytes(ctypes.byref(c), op))
+
+    def packed_bytes(self, which: int) -> int:
+        c = self.c()
+        return int(lib.moe_packed_bytes(ctypes.byref(c), which))
+
+    @classmethod
+    def of(cls, wl) -> "Problem":
+        """From a workload description with T, H, E, k, I, capacity, renormalize, dtype."""
+        return cls(wl.T, wl.H, wl.E, wl.k, wl.I, wl.capacity, wl.renormalize, wl.dtype)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _call(name: str, *args):
+    st = getattr(lib, name)(*args)
+    if st != MOE_OK:
+        raise MoeError(name, st)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def workspace(p: Problem, op: int, device="cuda") -> torch.Tensor:
+    """A workspace buffer for `op` (torch's allocator returns 256-byte aligned blocks)."""
+    return torch.empty(max(p.workspace_bytes(op), 256), dtype=torch.uint8, device=device)
+
+
+def pack_weights(p: Problem, w_gate, w_up, w_down, packed_gate_up=None, packed_down=None):
+    """One-time packing of [E,H,I], [E,H,I], [E,I,H] weights into the kernels' layout."""
+    dt = p.torch_dtype
+    _need(w_gate, "w_gate", (p.E, p.H, p.I), dt)
+    _need(w_up, "w_up", (p.E, p.H, p.I), dt)
+    _need(w_down, "w_down", (p.E, p.I, p.H), dt)
+    dev = w_gate.device
+    if packed_gate_up is None:
+        packed_gate_up = _empty((p.packed_bytes(W_GATE_UP),), torch.uint8, dev)
+    if packed_down is None:
+        packed_down = _empty((p.packed_bytes(W_DOWN),), torch.uint8, dev)
+    c = p.c()
+    _call("moe_pack_weights", ctypes.byref(c), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ptr(packed_gate_up), _ptr(packed_down), _stream())
+    return packed_gate_up, packed_down
+
+
+def route(p: Problem, logits, out=None, ws=None):
+    """Top-k + capacity: returns (topk_ids [T,k] i32, topk_w [T,k] f32, keep [T,k] u8)."""
+    _need(logits, "logits", (p.T, p.E), torch.float32)
+    dev = logits.device
+    ids, w, keep = out if out is not None else (
+        _empty((p.T, p.k), torch.int32, dev), _empty((p.T, p.k), torch.float32, dev),
+        _empty((p.T, p.k), torch.uint8, dev))
+    ws = workspace(p, OP_ROUTE, dev) if ws is None else ws
+    c = p.c()
+    _call("moe_route", ctypes.byref(c), _ptr(logits), _ptr(ids), _ptr(w), _ptr(keep), _ptr(ws),
+          ws.numel(), _stream())
+    return ids, w, keep
+
+
+def dispatch(p: Problem, x, topk_ids, keep=None, out=None, ws=None):
+    """Expert-contiguous layout + row gather.
+    Returns dict(counts, offsets, row_token, slot_to_row, xp)."""
+    dt = p.torch_dtype
+    _need(x, "x", (p.T, p.H), dt)
+    _need(topk_ids, "topk_ids", (p.T, p.k), torch.int32)
+    if keep is not None:
+        _need(keep, "keep", (p.T, p.k), torch.uint8)
+    dev = x.device
+    tk = p.T * p.k
+    if out is None:
+        out = dict(counts=_empty((p.E,), torch.int32, dev), offsets=_empty((p.E + 1,), torch.int32, dev),
+                   row_token=_empty((tk,), torch.int32, dev),
+                   slot_to_row=_empty((p.T, p.k), torch.int32, dev), xp=_empty((tk, p.H), dt, dev))
+    ws = workspace(p, OP_DISPATCH, dev) if ws is None else ws
+    c = p.c()
+    _call("moe_dispatch", ctypes.byref(c), _ptr(x), _ptr(topk_ids), _ptr(keep), _ptr(out["counts"]),
+          _ptr(out["offsets"]), _ptr(out["row_token"]), _ptr(out["slot_to_row"]), _ptr(out["xp"]),
+          _ptr(ws), ws.numel(), _stream())
+    return out
+
+
+def expert_gate_up(p: Problem, xp, offsets, packed_gate_up, out=None, ws=None):
+    """a = silu(xp Wg) * (xp Wu) per expert segment; returns a [T*k, I]."""
+    dt = p.torch_dtype
+    tk = p.T * p.k
+    _need(xp, "xp", (tk, p.H), dt)
+    _need(offsets, "offsets", (p.E + 1,), torch.int32)
+    a = _empty((tk, p.I), dt, xp.device) if out is None else out
+    ws = workspace(p, OP_FFN, xp.device) if ws is None else ws
+    c = p.c()
+    _call("moe_expert_gate_up", ctypes.byref(c), _ptr(xp), _ptr(offsets), _ptr(packed_gate_up),
+          _ptr(a), _ptr(ws), ws.numel(), _stream())
+    return a
+
+
+def expert_down(p: Problem, a, offsets, packed_down, out=None, ws=None):
+    """yp = a Wd per expert segment; returns yp [T*k, H]."""
+    dt = p.torch_dtype
+    tk = p.T * p.k
+    _need(a, "a", (tk, p.I), dt)
+    _need(offsets, "offsets", (p.E + 1,), torch.int32)
+    yp = _empty((tk, p.H), dt, a.device) if out is None else out
+    ws = workspace(p, OP_FFN, a.device) if ws is None else ws
+    c = p.c()
+    _call("moe_expert_down", ctypes.byref(c), _ptr(a), _ptr(offsets), _ptr(packed_down), _ptr(yp),
+          _ptr(ws), ws.numel(), _stream())
+    return yp
+
+
+def expert_ffn(p: Problem, xp, offsets, packed_gate_up, packed_down, out=None, ws=None):
+    """Grouped SwiGLU FFN; returns yp [T*k, H]."""
+    dt = p.torch_dtype
+    tk = p.T * p.k
+    _need(xp, "xp", (tk, p.H), dt)
+    _need(offsets, "offsets", (p.E + 1,), torch.int32)
+    yp = _empty((tk, p.H), dt, xp.device) if out is None else out
+    ws = workspace(p, OP_FFN, xp.device) if ws is None else ws
+    c = p.c()
+    _call("moe_expert_ffn", ctypes.byref(c), _ptr(xp), _ptr(offsets), _ptr(packed_gate_up),
+          _ptr(packed_down), _ptr(yp), _ptr(ws), ws.numel(), _stream())
+    return yp
+
+
+def combine(p: Problem, yp, topk_w, slot_to_row, out=None):
+    """y[t] = sum of kept w[t,j] * yp[slot_to_row[t,j]] in slot order; returns y [T, H]."""
+    dt = p.torch_dtype
+    _need(yp, "yp", (p.T * p.k, p.H), dt)
+    _need(topk_w, "topk_w", (p.T, p.k), torch.float32)
+    _need(slot_to_row, "slot_to_row", (p.T, p.k), torch.int32)
+    y = _empty((p.T, p.H), dt, yp.device) if out is None else out
+    c = p.c()
+    _call("moe_combine", ctypes.byref(c), _ptr(yp), _ptr(topk_w), _ptr(slot_to_row), _ptr(y),
+          _stream())
+    return y
+
+
+def layer(p: Problem, x, logits, packed_gate_up, packed_down, out=None, routing=None, ws=None):
+    """The whole layer.  `routing` may be a dict of preallocated buffers (topk_ids, topk_w,
+    keep, counts, offsets, row_token, slot_to_row) that receive the routing results."""
+    dt = p.torch_dtype
+    _need(x, "x", (p.T, p.H), dt)
+    _need(logits, "logits", (p.T, p.E), torch.float32)
+    y = _empty((p.T, p.H), dt, x.device) if out is None else out
+    r = routing or {}
+    ws = workspace(p, OP_LAYER, x.device) if ws is None else ws
+    c = p.c()
+    _call("moe_layer", ctypes.byref(c), _ptr(x), _ptr(logits), _ptr(packed_gate_up), _ptr(packed_down),
+          _ptr(y), _ptr(r.get("topk_ids")), _ptr(r.get("topk_w")), _ptr(r.get("keep")),
+          _ptr(r.get("counts")), _ptr(r.get("offsets")), _ptr(r.get("row_token")),
+          _ptr(r.get("slot_to_row")), _ptr(ws), ws.numel(), _stream())
+    return y
+
+
+def routing_buffers(p: Problem, device="cuda"):
+    """Preallocated routing outputs for layer(..., routing=...)."""
+    tk = p.T * p.k
+    return dict(topk_ids=_empty((p.T, p.k), torch.int32, device),
+                topk_w=_empty((p.T, p.k), torch.float32, device),
+                keep=_empty((p.T, p.k), torch.uint8, device),
+                counts=_empty((p.E,), torch.int32, device),
+                offsets=_empty((p.E + 1,), torch.int32, device),
+                row_token=_empty((tk,), torch.int32, device),
+                slot_to_row=_empty((p.T, p.k), torch.int32, device))

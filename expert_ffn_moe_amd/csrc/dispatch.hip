@@ -1,0 +1,278 @@
+// Local dispatch: per-expert capacity, expert histogram + prefix scan, stable scatter and
+// row gather.
+//
+// Layout (LightLLM PR #1687, PR body: the grouped GEMM runs on the expert prefix-sum
+// layout): rows of expert e occupy [offsets[e], offsets[e+1]) with offsets the exclusive
+// scan of the per-expert counts; inside a segment rows ascend in token index.  On one GPU
+// this permutation stands in for the dispatch all-to-all (research-vault WideEP card).
+//
+// Capacity (docs.axolotl.ai expert-parallel args, `expert_parallel_token_capacity`): an
+// expert with more than C candidate assignments keeps the C with the largest
+// (weight, -token) key; the rest are dropped.
+//
+// Determinism: every count comes from popcounts of per-chunk bitmaps (one bit per token
+// of a 64-token chunk), every rank from a popcount of the bits below the token, every
+// sum from a fixed-order scan.  LDS atomics only set bits or count into a histogram,
+// whose results do not depend on their order.
+#include "moe_internal.h"
+#include "wave.h"
+
+namespace moe {
+namespace {
+
+// Builds, for the chunk of 64 tokens handled by this wavefront, the bitmap
+// bm[e] = {lanes whose token has a (kept) slot routed to e}.  Call from all threads of
+// the block (contains barriers).
+template <bool HAS_KEEP>
+__device__ __forceinline__ void build_chunk_bitmap(uint64_t* bm, const int32_t* __restrict__ ids,
+                                                   const uint8_t* __restrict__ keep, int T,
+                                                   int E, int k, int c, int nchunks) {
+  const int lane = threadIdx.x & 63;
+  for (int e = lane; e < E; e += 64) bm[e] = 0;
+  __syncthreads();
+  const int t = c * kChunk + lane;
+  if (c < nchunks && t < T) {
+    for (int j = 0; j < k; ++j) {
+      const size_t s = (size_t)t * k + j;
+      if (!HAS_KEEP || keep[s]) atomicOr((unsigned long long*)&bm[ids[s]], 1ull << lane);
+    }
+  }
+  __syncthreads();
+}
+
+template <bool HAS_KEEP>
+__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ ids,
+                                                         const uint8_t* __restrict__ keep, int T,
+                                                         int E, int k, int nchunks,
+                                                         int32_t* __restrict__ chunk_hist) {
+  extern __shared__ uint64_t smem_bm[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  uint64_t* bm = smem_bm + (size_t)wave * E;
+  build_chunk_bitmap<HAS_KEEP>(bm, ids, keep, T, E, k, c, nchunks);
+  if (c < nchunks)
+    for (int e = lane; e < E; e += 64) chunk_hist[(size_t)c * E + e] = __popcll(bm[e]);
+}
+
+// Column scan: 64 experts per block (one per lane), 16 wavefronts split the chunks.
+__global__ __launch_bounds__(1024) void scan_cols_kernel(const int32_t* __restrict__ chunk_hist,
+                                                         int E, int nchunks,
+                                                         int32_t* __restrict__ chunk_base,
+                                                         int32_t* __restrict__ counts) {
+  __shared__ int part[16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + lane;
+  const int per = div_up(nchunks, 16);
+  const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
+  int sum = 0;
+  if (e < E)
+    for (int c = c0; c < c1; ++c) sum += chunk_hist[(size_t)c * E + e];
+  part[wave][lane] = sum;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += part[w][lane];
+  if (e < E) {
+    for (int c = c0; c < c1; ++c) {
+      const int v = chunk_hist[(size_t)c * E + e];
+      chunk_base[(size_t)c * E + e] = base;
+      base += v;
+    }
+    if (wave == 15) counts[e] = base;
+  }
+}
+
+// offsets = exclusive scan of counts (E <= 1024, one block).
+__global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __restrict__ counts,
+                                                            int E,
+                                                            int32_t* __restrict__ offsets) {
+  __shared__ int wsum[16];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = threadIdx.x;
+  const int v = e < E ? counts[e] : 0;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) wsum[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  if (e < E) offsets[e] = base + inc - v;
+  if (e == E - 1) offsets[E] = base + inc;
+}
+
+template <bool HAS_KEEP, bool CAND>
+__global__ __launch_bounds__(256) void scatter_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ keep, int T, int E, int k,
+    int nchunks, const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ slot_to_row,
+    int32_t* __restrict__ cand_slot) {
+  extern __shared__ uint64_t smem_bm[];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + wave;
+  uint64_t* bm = smem_bm + (size_t)wave * E;
+  build_chunk_bitmap<HAS_KEEP>(bm, ids, keep, T, E, k, c, nchunks);
+  const int t = c * kChunk + lane;
+  if (c >= nchunks || t >= T) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j = 0; j < k; ++j) {
+    const size_t s = (size_t)t * k + j;
+    const int e = ids[s];
+    if (!HAS_KEEP || keep[s]) {
+      const int row = offsets[e] + chunk_base[(size_t)c * E + e] + __popcll(bm[e] & below);
+      if (CAND) {
+        cand_slot[row] = (int32_t)s;
+      } else {
+        row_token[row] = t;
+        slot_to_row[s] = row;
+      }
+    } else if (!CAND) {
+      slot_to_row[s] = -1;
+    }
+  }
+}
+
+// Capacity selection, one block per expert.  Keys (weight bits << 32) | (~token) are
+// unique per expert and order like (weight desc, token asc) when compared as unsigned
+// integers (weights are >= 0).  An MSD radix select over 8-bit digits finds the
+// C-th largest key; every key below it is dropped.
+__device__ __forceinline__ uint64_t cap_key(const float* __restrict__ w, int32_t slot, int k) {
+  const uint32_t wb = __float_as_uint(w[slot]);
+  const uint32_t t = (uint32_t)(slot / k);
+  return ((uint64_t)wb << 32) | (uint32_t)(0xFFFFFFFFu - t);
+}
+
+__global__ __launch_bounds__(512) void capacity_select_kernel(
+    const int32_t* __restrict__ cand_counts, const int32_t* __restrict__ cand_offsets,
+    const int32_t* __restrict__ cand_slot, const float* __restrict__ w, int k, int C,
+    uint8_t* __restrict__ keep) {
+  __shared__ uint32_t hist[256];
+  __shared__ unsigned long long s_prefix;
+  __shared__ int s_need, s_done;
+  const int e = blockIdx.x;
+  const int cnt = cand_counts[e];
+  if (cnt <= C) return;  // block-uniform
+  const int32_t* slots = cand_slot + cand_offsets[e];
+  uint64_t prefix = 0, mask = 0;
+  int need = C;
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+      const uint64_t key = cap_key(w, slots[i], k);
+      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t acc = 0;
+      int sel = 0;
+      for (int d = 255; d >= 0; --d) {
+        if (acc + hist[d] >= (uint32_t)need) {
+          sel = d;
+          break;
+        }
+        acc += hist[d];
+      }
+      need -= (int)acc;
+      prefix |= (uint64_t)sel << shift;
+      s_prefix = prefix;
+      s_need = need;
+      s_done = (hist[sel] == (uint32_t)need);
+    }
+    __syncthreads();
+    prefix = s_prefix;
+    need = s_need;
+    mask |= (uint64_t)0xFF << shift;
+    const int done = s_done;
+    __syncthreads();
+    if (done) break;
+  }
+  // keys >= prefix (the lower bits of prefix are zero) are exactly the C largest
+  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
+    const int32_t s = slots[i];
+    if (cap_key(w, s, k) < prefix) keep[s] = 0;
+  }
+}
+
+// One token per block: read x[t] once, write it to each of its rows.
+__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
+                                                     const int32_t* __restrict__ slot_to_row,
+                                                     int k, int nvec, uint4* __restrict__ xp) {
+  __shared__ int rows[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) rows[threadIdx.x] = slot_to_row[(size_t)t * k + threadIdx.x];
+  __syncthreads();
+  for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
+    const uint4 d = x[(size_t)t * nvec + v];
+    for (int j = 0; j < k; ++j) {
+      const int r = rows[j];
+      if (r >= 0) xp[(size_t)r * nvec + v] = d;
+    }
+  }
+}
+
+inline size_t bitmap_lds(const moe_problem& p) { return (size_t)4 * p.E * sizeof(uint64_t); }
+
+}  // namespace
+
+hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                             int32_t* chunk_hist, hipStream_t s) {
+  const int nchunks = div_up(p.T, kChunk);
+  dim3 grid(div_up(nchunks, 4));
+  if (keep)
+    hipLaunchKernelGGL(chunk_hist_kernel<true>, grid, dim3(256), bitmap_lds(p), s, ids, keep,
+                       p.T, p.E, p.k, nchunks, chunk_hist);
+  else
+    hipLaunchKernelGGL(chunk_hist_kernel<false>, grid, dim3(256), bitmap_lds(p), s, ids, keep,
+                       p.T, p.E, p.k, nchunks, chunk_hist);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
+                       int32_t* counts, int32_t* offsets, hipStream_t s) {
+  const int nchunks = div_up(p.T, kChunk);
+  hipLaunchKernelGGL(scan_cols_kernel, dim3(div_up(p.E, 64)), dim3(1024), 0, s, chunk_hist,
+                     p.E, nchunks, chunk_base, counts);
+  hipLaunchKernelGGL(scan_experts_kernel, dim3(1), dim3(1024), 0, s, counts, p.E, offsets);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                          const int32_t* chunk_base, const int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
+                          hipStream_t s) {
+  const int nchunks = div_up(p.T, kChunk);
+  dim3 grid(div_up(nchunks, 4));
+  const size_t lds = bitmap_lds(p);
+  if (cand_slot) {
+    hipLaunchKernelGGL((scatter_kernel<false, true>), grid, dim3(256), lds, s, ids, keep, p.T,
+                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
+                       cand_slot);
+  } else if (keep) {
+    hipLaunchKernelGGL((scatter_kernel<true, false>), grid, dim3(256), lds, s, ids, keep, p.T,
+                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
+                       cand_slot);
+  } else {
+    hipLaunchKernelGGL((scatter_kernel<false, false>), grid, dim3(256), lds, s, ids, keep, p.T,
+                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
+                       cand_slot);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
+                                  const int32_t* cand_offsets, const int32_t* cand_slot,
+                                  const float* topk_w, uint8_t* keep, hipStream_t s) {
+  hipLaunchKernelGGL(capacity_select_kernel, dim3(p.E), dim3(512), 0, s, cand_counts,
+                     cand_offsets, cand_slot, topk_w, p.k, p.capacity, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slot_to_row,
+                         void* xp, hipStream_t s) {
+  const size_t row_bytes = (size_t)p.H * (p.act_dtype == MOE_BF16 ? 2 : 4);
+  const int nvec = (int)(row_bytes / 16);
+  hipLaunchKernelGGL(gather_kernel, dim3(p.T), dim3(256), 0, s, (const uint4*)x, slot_to_row,
+                     p.k, nvec, (uint4*)xp);
+  return hipGetLastError();
+}
+
+}  // namespace moe

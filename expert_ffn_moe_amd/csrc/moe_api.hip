@@ -1,0 +1,340 @@
+// C ABI entry points: argument checks, workspace carving and kernel sequencing.  Every
+// step of the path runs in the kernels of this library; there is no other implementation
+// to fall back to.
+#include <hip/hip_runtime.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+RankScratch carve_rank(Carve& c, const moe_problem& p, bool with_capacity) {
+  const size_t nchunks = (size_t)div_up(p.T, kChunk);
+  RankScratch r{};
+  r.chunk_hist = c.take<int32_t>(nchunks * p.E);
+  r.chunk_base = c.take<int32_t>(nchunks * p.E);
+  if (with_capacity) {
+    r.cand_counts = c.take<int32_t>(p.E);
+    r.cand_offsets = c.take<int32_t>((size_t)p.E + 1);
+    r.cand_slot = c.take<int32_t>((size_t)p.T * p.k);
+  }
+  return r;
+}
+
+TileTable carve_tiles(Carve& c, const moe_problem& p) {
+  TileTable t{};
+  t.max_tiles = div_up(p.T * p.k, kPrefillBM) + p.E;
+  t.tile_count = c.take<int32_t>(1);
+  t.tile_expert = c.take<int32_t>(t.max_tiles);
+  t.tile_row0 = c.take<int32_t>(t.max_tiles);
+  return t;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+size_t elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace of the FFN: the intermediate activation plus the tile table.
+struct FfnScratch {
+  void* a;
+  TileTable tt;
+};
+FfnScratch carve_ffn(Carve& c, const moe_problem& p) {
+  FfnScratch f{};
+  f.a = c.take<char>((size_t)p.T * p.k * p.I * elem_bytes(p.act_dtype));
+  f.tt = carve_tiles(c, p);
+  return f;
+}
+
+struct LayerScratch {
+  int32_t *ids, *counts, *offsets, *row_token, *slot_to_row;
+  float* w;
+  uint8_t* keep;
+  void *xp, *yp;
+  RankScratch rank;
+  FfnScratch ffn;
+};
+LayerScratch carve_layer(Carve& c, const moe_problem& p) {
+  const size_t tk = (size_t)p.T * p.k;
+  const size_t eb = elem_bytes(p.act_dtype);
+  LayerScratch L{};
+  L.ids = c.take<int32_t>(tk);
+  L.w = c.take<float>(tk);
+  L.keep = c.take<uint8_t>(tk);
+  L.counts = c.take<int32_t>(p.E);
+  L.offsets = c.take<int32_t>((size_t)p.E + 1);
+  L.row_token = c.take<int32_t>(tk);
+  L.slot_to_row = c.take<int32_t>(tk);
+  L.xp = c.take<char>(tk * p.H * eb);
+  L.yp = c.take<char>(tk * p.H * eb);
+  L.rank = carve_rank(c, p, p.capacity > 0);
+  L.ffn = carve_ffn(c, p);
+  return L;
+}
+
+size_t ws_bytes_of(const moe_problem& p, int op) {
+  Carve c(nullptr);
+  switch (op) {
+    case MOE_OP_ROUTE:
+      if (p.capacity > 0) carve_rank(c, p, true);
+      break;
+    case MOE_OP_DISPATCH:
+      carve_rank(c, p, false);
+      break;
+    case MOE_OP_FFN:
+      carve_ffn(c, p);
+      break;
+    case MOE_OP_COMBINE:
+      break;
+    case MOE_OP_LAYER:
+      carve_layer(c, p);
+      break;
+    default:
+      return 0;
+  }
+  return c.used;
+}
+
+int check_ws(const moe_problem* p, int op, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_of(*p, op);
+  if (need == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return MOE_ERR_INVALID_ARG;
+  return ws_bytes < need ? MOE_ERR_WORKSPACE : MOE_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// The routing pipeline: top-k, then (with a cap) candidate layout + radix select.
+hipError_t run_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                     uint8_t* keep, const RankScratch& r, hipStream_t s) {
+  hipError_t err = launch_route(p, logits, ids, w, keep, s);
+  if (err != hipSuccess || p.capacity <= 0) return err;
+  if ((err = launch_chunk_hist(p, ids, nullptr, r.chunk_hist, s)) != hipSuccess) return err;
+  if ((err = launch_scan(p, r.chunk_hist, r.chunk_base, r.cand_counts, r.cand_offsets, s)) !=
+      hipSuccess)
+    return err;
+  if ((err = launch_scatter(p, ids, nullptr, r.chunk_base, r.cand_offsets, nullptr, nullptr,
+                            r.cand_slot, s)) != hipSuccess)
+    return err;
+  return launch_capacity_select(p, r.cand_counts, r.cand_offsets, r.cand_slot, w, keep, s);
+}
+
+hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
+                        const uint8_t* keep, int32_t* counts, int32_t* offsets,
+                        int32_t* row_token, int32_t* slot_to_row, void* xp,
+                        const RankScratch& r, hipStream_t s) {
+  hipError_t err = launch_chunk_hist(p, ids, keep, r.chunk_hist, s);
+  if (err == hipSuccess) err = launch_scan(p, r.chunk_hist, r.chunk_base, counts, offsets, s);
+  if (err == hipSuccess)
+    err = launch_scatter(p, ids, keep, r.chunk_base, offsets, row_token, slot_to_row, nullptr,
+                         s);
+  if (err == hipSuccess) err = launch_gather(p, x, slot_to_row, xp, s);
+  return err;
+}
+
+hipError_t run_gate_up(const moe_problem& p, const void* xp, const int32_t* offsets,
+                       const void* pgu, void* a, const TileTable& tt, bool need_table,
+                       hipStream_t s) {
+  if (p.act_dtype == MOE_F32) {
+    const size_t n = (size_t)p.E * p.H * p.I;
+    return launch_gate_up_f32(p, (const float*)xp, offsets, (const float*)pgu,
+                              (const float*)pgu + n, (float*)a, s);
+  }
+  if (need_table && !ffn_use_decode(p)) {
+    hipError_t err = launch_tile_table(p, offsets, tt, s);
+    if (err != hipSuccess) return err;
+  }
+  return launch_gate_up_bf16(p, xp, offsets, pgu, a, tt, s);
+}
+
+hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
+                    const void* pd, void* yp, const TileTable& tt, bool need_table,
+                    hipStream_t s) {
+  if (p.act_dtype == MOE_F32)
+    return launch_down_f32(p, (const float*)a, offsets, (const float*)pd, (float*)yp, s);
+  if (need_table && !ffn_use_decode(p)) {
+    hipError_t err = launch_tile_table(p, offsets, tt, s);
+    if (err != hipSuccess) return err;
+  }
+  return launch_down_bf16(p, a, offsets, pd, yp, tt, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported problem";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int moe_problem_check(const moe_problem* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->T < 1 || p->H < 1 || p->E < 1 || p->k < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
+  if (p->k > p->E) return MOE_ERR_INVALID_ARG;
+  if ((p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) ||
+      (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16))
+    return MOE_ERR_INVALID_ARG;
+  if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
+  if (p->E > 1024 || p->k > 32) return MOE_ERR_UNSUPPORTED;
+  if (p->act_dtype != p->w_dtype) return MOE_ERR_UNSUPPORTED;
+  const int mult = p->act_dtype == MOE_BF16 ? 64 : 8;
+  if (p->H % mult || p->I % mult) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->T * p->k >= ((int64_t)1 << 31) - 2 * (int64_t)kPrefillBM * 1024)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_problem* p, int op) {
+  if (moe_problem_check(p) != MOE_OK) return 0;
+  return ws_bytes_of(*p, op);
+}
+
+size_t moe_packed_bytes(const moe_problem* p, int which) {
+  if (moe_problem_check(p) != MOE_OK) return 0;
+  const size_t n = (size_t)p->E * p->H * p->I * elem_bytes(p->w_dtype);
+  if (which == MOE_W_GATE_UP) return 2 * n;
+  if (which == MOE_W_DOWN) return n;
+  return 0;
+}
+
+int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                     const void* w_down, void* packed_gate_up, void* packed_down,
+                     void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!w_gate || !w_up || !w_down || !packed_gate_up || !packed_down)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed_gate_up) || !aligned16(packed_down)) return MOE_ERR_INVALID_ARG;
+  return status_of(
+      launch_pack(*p, w_gate, w_up, w_down, packed_gate_up, packed_down, as_stream(stream)));
+}
+
+int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
+              uint8_t* keep, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w || !keep) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  RankScratch r = carve_rank(c, *p, p->capacity > 0);
+  return status_of(run_route(*p, logits, topk_ids, topk_w, keep, r, as_stream(stream)));
+}
+
+int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                 const uint8_t* keep, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                 int32_t* slot_to_row, void* xp, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!x || !topk_ids || !counts || !offsets || !row_token || !slot_to_row || !xp)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xp)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_DISPATCH, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  RankScratch r = carve_rank(c, *p, false);
+  return status_of(run_dispatch(*p, x, topk_ids, keep, counts, offsets, row_token, slot_to_row,
+                                xp, r, as_stream(stream)));
+}
+
+int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offsets,
+                       const void* packed_gate_up, void* a, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!xp || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  FfnScratch f = carve_ffn(c, *p);
+  return status_of(run_gate_up(*p, xp, offsets, packed_gate_up, a, f.tt, true,
+                               as_stream(stream)));
+}
+
+int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
+                    const void* packed_down, void* yp, void* ws, size_t ws_bytes,
+                    void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!a || !offsets || !packed_down || !yp) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(a) || !aligned16(packed_down) || !aligned16(yp)) return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  FfnScratch f = carve_ffn(c, *p);
+  return status_of(run_down(*p, a, offsets, packed_down, yp, f.tt, true, as_stream(stream)));
+}
+
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
+                   const void* packed_gate_up, const void* packed_down, void* yp, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!xp || !offsets || !packed_gate_up || !packed_down || !yp) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(packed_down) ||
+      !aligned16(yp))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  FfnScratch f = carve_ffn(c, *p);
+  hipStream_t s = as_stream(stream);
+  hipError_t err = run_gate_up(*p, xp, offsets, packed_gate_up, f.a, f.tt, true, s);
+  if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, f.tt, false, s);
+  return status_of(err);
+}
+
+int moe_combine(const moe_problem* p, const void* yp, const float* topk_w,
+                const int32_t* slot_to_row, void* y, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!yp || !topk_w || !slot_to_row || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(yp) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  return status_of(launch_combine(*p, yp, topk_w, slot_to_row, y, as_stream(stream)));
+}
+
+int moe_layer(const moe_problem* p, const void* x, const float* logits,
+              const void* packed_gate_up, const void* packed_down, void* y, int32_t* topk_ids,
+              float* topk_w, uint8_t* keep, int32_t* counts, int32_t* offsets,
+              int32_t* row_token, int32_t* slot_to_row, void* ws, size_t ws_bytes,
+              void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!x || !logits || !packed_gate_up || !packed_down || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(packed_gate_up) || !aligned16(packed_down))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_LAYER, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  LayerScratch L = carve_layer(c, *p);
+  if (!topk_ids) topk_ids = L.ids;
+  if (!topk_w) topk_w = L.w;
+  if (!keep) keep = L.keep;
+  if (!counts) counts = L.counts;
+  if (!offsets) offsets = L.offsets;
+  if (!row_token) row_token = L.row_token;
+  if (!slot_to_row) slot_to_row = L.slot_to_row;
+  hipStream_t s = as_stream(stream);
+  hipError_t err = run_route(*p, logits, topk_ids, topk_w, keep, L.rank, s);
+  if (err == hipSuccess)
+    err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
+                       row_token, slot_to_row, L.xp, L.rank, s);
+  if (err == hipSuccess)
+    err = run_gate_up(*p, L.xp, offsets, packed_gate_up, L.ffn.a, L.ffn.tt, true, s);
+  if (err == hipSuccess)
+    err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, L.ffn.tt, false, s);
+  if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, y, s);
+  return status_of(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Internal launchers of the MoE hot-path kernels (gfx950).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Tokens per routing chunk: one wavefront, one bit per token in a 64-bit mask.
+constexpr int kChunk = 64;
+// Rows per M tile of the prefill grouped GEMM.
+constexpr int kPrefillBM = 128;
+
+__host__ __device__ inline int div_up(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Bump allocator over a caller-provided workspace (sizes are rounded to 256 bytes).
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+// Scratch of the routing/dispatch pipeline.
+struct RankScratch {
+  int32_t* chunk_hist;   // [nchunks, E]
+  int32_t* chunk_base;   // [nchunks, E]
+  int32_t* cand_counts;  // [E]      (capacity only)
+  int32_t* cand_offsets; // [E + 1]  (capacity only)
+  int32_t* cand_slot;    // [T * k]  (capacity only)
+};
+RankScratch carve_rank(Carve& c, const moe_problem& p, bool with_capacity);
+
+// Tile table of the prefill grouped GEMM: tile i covers rows [row0, row0 + 128) of
+// expert tile_expert[i]; tile_count[0] tiles in total.
+struct TileTable {
+  int32_t* tile_count;   // [1]
+  int32_t* tile_expert;  // [max_tiles]
+  int32_t* tile_row0;    // [max_tiles]
+  int max_tiles;
+};
+TileTable carve_tiles(Carve& c, const moe_problem& p);
+
+// ---- route.hip
+hipError_t launch_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+                        uint8_t* keep, hipStream_t s);
+
+// ---- dispatch.hip
+// Per-chunk histogram of (kept) assignments per expert.
+hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                             int32_t* chunk_hist, hipStream_t s);
+// Column scan over chunks per expert -> chunk_base, counts; then offsets = scan(counts).
+hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
+                       int32_t* counts, int32_t* offsets, hipStream_t s);
+// Stable scatter: row of each kept slot.  If cand_slot != NULL the rows index the slot
+// list cand_slot (capacity candidates) instead of writing row_token / slot_to_row.
+hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                          const int32_t* chunk_base, const int32_t* offsets,
+                          int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
+                          hipStream_t s);
+// Capacity: per overflowing expert, radix-select the top-C keys and clear keep for the rest.
+hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
+                                  const int32_t* cand_offsets, const int32_t* cand_slot,
+                                  const float* topk_w, uint8_t* keep, hipStream_t s);
+// Row gather xp[slot_to_row[t, j]] = x[t].
+hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slot_to_row,
+                         void* xp, hipStream_t s);
+
+// ---- combine.hip
+hipError_t launch_combine(const moe_problem& p, const void* yp, const float* w,
+                          const int32_t* slot_to_row, void* y, hipStream_t s);
+
+// ---- pack.hip
+hipError_t launch_pack(const moe_problem& p, const void* wg, const void* wu, const void* wd,
+                       void* packed_gu, void* packed_d, hipStream_t s);
+
+// ---- ffn_bf16.hip / ffn_f32.hip
+bool ffn_use_decode(const moe_problem& p);
+hipError_t launch_tile_table(const moe_problem& p, const int32_t* offsets, TileTable tt,
+                             hipStream_t s);
+hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32_t* offsets,
+                               const void* packed_gu, void* a, TileTable tt, hipStream_t s);
+hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
+                            const void* packed_d, void* yp, TileTable tt, hipStream_t s);
+hipError_t launch_gate_up_f32(const moe_problem& p, const float* xp, const int32_t* offsets,
+                              const float* wg, const float* wu, float* a, hipStream_t s);
+hipError_t launch_down_f32(const moe_problem& p, const float* a, const int32_t* offsets,
+                           const float* wd, float* yp, hipStream_t s);
+
+}  // namespace moe

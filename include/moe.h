@@ -1,0 +1,206 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path: one GPU's share of an
+ * expert-parallel mixture-of-experts layer.
+ *
+ *   moe_route        top-k routing + per-expert capacity           (route)
+ *   moe_dispatch     expert-contiguous permutation of token rows   (local dispatch)
+ *   moe_expert_ffn   grouped SwiGLU FFN = moe_expert_gate_up + moe_expert_down
+ *   moe_combine      weighted sum of each token's expert rows     (combine)
+ *   moe_layer        all of the above on one stream
+ *
+ * The pages describe the operations in prose; each declaration names the passage:
+ *   [axolotl]  docs.axolotl.ai "integrations.expert_parallel.args", attribute table
+ *              (row `expert_parallel_token_capacity`; function
+ *              `validate_expert_parallel_topology`).
+ *   [LightLLM] LightLLM PR #1687 page: the PR body's call-order paragraph (top-k in the
+ *              logical expert space, `norm_topk_prob`, `experts()` versus
+ *              `experts_with_topk()`, expert prefix-sum layout for the grouped GEMM,
+ *              `silu_and_mul` after the gate/up GEMM) and the walkthrough table row
+ *              "Synchronous prefill and decode execution" (decode reduces expert outputs
+ *              into dense output).
+ *   [WideEP]   research-vault claim card, "Evidence": pure DP+EP has one communication
+ *              pattern, the all-to-all that routes tokens to experts.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device), row-major,
+ *     contiguous.  `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on `stream` and returns; nothing synchronises the host, nothing
+ *     allocates or frees device memory, no state survives between calls.
+ *   - The caller owns every buffer, including the workspace `ws` of at least
+ *     moe_workspace_bytes(p, op) bytes (256-byte aligned).  Row buffers (row_token, xp,
+ *     yp) hold T*k rows: the number of kept assignments N is only known on the device.
+ *   - Errors are reported synchronously, before anything is enqueued:
+ *       MOE_ERR_INVALID_ARG  NULL required pointer, non-positive sizes, k > E, unknown
+ *                            dtype, misaligned pointer;
+ *       MOE_ERR_UNSUPPORTED  a valid problem the kernels do not handle (see
+ *                            moe_problem_check);
+ *       MOE_ERR_WORKSPACE    ws_bytes < moe_workspace_bytes(p, op);
+ *       MOE_ERR_HIP          a launch failed (hipGetLastError after enqueueing).
+ *     No call ever falls back to another implementation.
+ *   - Device-side preconditions (not checked): logits finite; caller-supplied ids in
+ *     [0, E) and distinct within a token; input and output buffers do not overlap.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Problem description.  T tokens of width H, E experts, top-k, SwiGLU width I. */
+typedef struct {
+  int32_t T, H, E, k, I;
+  /* Max (token, expert) assignments per expert per call; <= 0 means no cap
+   * ([axolotl] `expert_parallel_token_capacity`, None = no cap). */
+  int32_t capacity;
+  /* 1: the top-k weights are renormalised to sum to 1 ([LightLLM] `norm_topk_prob`);
+   * 0: they are the plain softmax probabilities over all E experts. */
+  int32_t renormalize;
+  int32_t act_dtype; /* moe_dtype of x, xp, the intermediate activation, yp, y */
+  int32_t w_dtype;   /* moe_dtype of the expert weights */
+} moe_problem;
+
+typedef enum {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_DISPATCH = 1,
+  MOE_OP_FFN = 2, /* moe_expert_ffn, moe_expert_gate_up and moe_expert_down */
+  MOE_OP_COMBINE = 3,
+  MOE_OP_LAYER = 4
+} moe_op;
+
+typedef enum { MOE_W_GATE_UP = 0, MOE_W_DOWN = 1 } moe_weight_set;
+
+/* Text for a status code (static storage). */
+const char* moe_status_str(int status);
+
+/* Host-only validation of a problem ([axolotl] `validate_expert_parallel_topology`:
+ * layouts the kernels do not handle are rejected up front, never run another way).
+ * Returns MOE_OK, MOE_ERR_INVALID_ARG (p NULL, T/H/E/k/I < 1, k > E, dtype unknown) or
+ * MOE_ERR_UNSUPPORTED: E > 1024, k > 32, act_dtype != w_dtype, H or I not a multiple
+ * of 64 (bf16) or 8 (f32), T*k >= 2^31. */
+int moe_problem_check(const moe_problem* p);
+
+/* Workspace bytes that `op` needs for problem p (0 if p is invalid). */
+size_t moe_workspace_bytes(const moe_problem* p, int op);
+
+/* ---------------------------------------------------------------------------------
+ * Expert weights.  The natural layout is W_gate, W_up: [E, H, I] and W_down: [E, I, H]
+ * (row-major, y = x W).  The kernels read a packed copy in which every 32-column by
+ * 16-row block of a weight matrix is one contiguous 1 KiB matrix-core operand (the
+ * reduction dimension contiguous in 8-element runs, as the pages' grouped GEMMs take
+ * their weights "nt").  Packing is a one-time step when weights are loaded, like any
+ * checkpoint layout conversion; the packed buffers stay resident and are what
+ * moe_expert_ffn and moe_layer read.
+ *
+ * moe_packed_bytes: size of one packed set (MOE_W_GATE_UP holds gate and up).
+ * moe_pack_weights: writes packed_gate_up (E*2*H*I elements) and packed_down
+ *   (E*I*H elements) from the natural layout; elements are copied bit for bit.
+ *   For f32 problems the packed layout is the natural layout.
+ * --------------------------------------------------------------------------------- */
+size_t moe_packed_bytes(const moe_problem* p, int which);
+int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
+                     const void* w_down, void* packed_gate_up, void* packed_down,
+                     void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route -- [LightLLM] call-order paragraph: top-k chosen in the logical expert
+ * space, weights optionally renormalised; [axolotl] capacity row: at most `capacity`
+ * assignments per expert, the lowest-weight excess dropped.
+ *
+ *   logits   [T, E] f32   router logits (input, finite)
+ *   topk_ids [T, k] i32   expert ids, slot order = logit descending, ties to the
+ *                         lower expert id
+ *   topk_w   [T, k] f32   softmax weights of the chosen experts (renormalised to sum
+ *                         to 1 if p->renormalize); computed with a specified fp32
+ *                         arithmetic so they are reproducible bit for bit
+ *   keep     [T, k] u8    1 = kept, 0 = dropped by the capacity (all 1 without a cap).
+ *                         Order for dropping: weight ascending, ties: higher token
+ *                         index dropped first.  Dropped slots keep their weight in
+ *                         topk_w; they are not re-routed.
+ * --------------------------------------------------------------------------------- */
+int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
+              uint8_t* keep, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_dispatch -- [LightLLM] expert prefix-sum layout (`use_psum_layout`); [WideEP]:
+ * on one GPU the dispatch all-to-all becomes this permutation.  Accepts caller routing
+ * ([LightLLM] `experts_with_topk`).
+ *
+ *   x           [T, H]    act dtype  token rows
+ *   topk_ids    [T, k]    i32
+ *   keep        [T, k]    u8 or NULL (NULL: all kept)
+ *   counts      [E]       i32  kept assignments per expert            (output)
+ *   offsets     [E+1]     i32  exclusive scan of counts, offsets[E]=N (output)
+ *   row_token   [T*k]     i32  token of row r for r < N; rows of an expert are
+ *                              contiguous and in ascending token order (output)
+ *   slot_to_row [T, k]    i32  row of slot (t, j), -1 if dropped        (output)
+ *   xp          [T*k, H]  act dtype  xp[r] = x[row_token[r]] for r < N  (output)
+ * All integer outputs are deterministic (no atomics-order effects).
+ * --------------------------------------------------------------------------------- */
+int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
+                 const uint8_t* keep, int32_t* counts, int32_t* offsets, int32_t* row_token,
+                 int32_t* slot_to_row, void* xp, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * Grouped SwiGLU expert FFN over the prefix-sum layout ([LightLLM]: grouped GEMM, then
+ * `silu_and_mul`).  For each expert e and each of its rows r in
+ * [offsets[e], offsets[e+1]):
+ *   a[r]  = silu(xp[r] Wg[e]) * (xp[r] Wu[e]),   silu(z) = z / (1 + exp(-z))
+ *   yp[r] = a[r] Wd[e]
+ * fp32 accumulation; `a` and yp are stored in the activation dtype.  offsets are read
+ * on the device (no host synchronisation); rows >= offsets[E] are not touched.
+ *
+ *   xp [T*k, H], a [T*k, I], yp [T*k, H] (act dtype); offsets [E+1] i32;
+ *   packed_gate_up / packed_down from moe_pack_weights.
+ * moe_expert_ffn keeps `a` in the workspace; the two halves are also callable alone.
+ * --------------------------------------------------------------------------------- */
+int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
+                   const void* packed_gate_up, const void* packed_down, void* yp, void* ws,
+                   size_t ws_bytes, void* stream);
+int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offsets,
+                       const void* packed_gate_up, void* a, void* ws, size_t ws_bytes,
+                       void* stream);
+int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
+                    const void* packed_down, void* yp, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_combine -- [LightLLM] walkthrough, "Synchronous prefill and decode execution":
+ * expert outputs are reduced back into dense token order.
+ *   y[t] = sum over j = 0..k-1 with slot_to_row[t,j] >= 0 of topk_w[t,j] * yp[row]
+ * summed in fp32 in slot order (deterministic, no atomics), stored in the act dtype.
+ * A token whose slots were all dropped gets 0.
+ *   yp [T*k, H], topk_w [T, k] f32, slot_to_row [T, k] i32, y [T, H].
+ * --------------------------------------------------------------------------------- */
+int moe_combine(const moe_problem* p, const void* yp, const float* topk_w,
+                const int32_t* slot_to_row, void* y, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_layer -- route, capacity, dispatch, FFN and combine in one call on one stream.
+ * x [T, H], logits [T, E] f32, packed weights, y [T, H].  The routing outputs are
+ * optional: pass NULL to keep them in the workspace, or buffers of the shapes above to
+ * receive them.
+ * --------------------------------------------------------------------------------- */
+int moe_layer(const moe_problem* p, const void* x, const float* logits,
+              const void* packed_gate_up, const void* packed_down, void* y,
+              int32_t* topk_ids, float* topk_w, uint8_t* keep, int32_t* counts,
+              int32_t* offsets, int32_t* row_token, int32_t* slot_to_row, void* ws,
+              size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,99 @@
+"""The C-ABI library: it loads, exports every entry point include/moe.h declares, and its
+host-side checks (problem validation, workspace and packed sizes) behave as documented.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import expert_ffn_moe_amd
+
+    return expert_ffn_moe_amd
+
+
+def test_library_exports_every_declared_symbol(moe):
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(moe.lib, n), n
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_library_is_built_for_gfx950():
+    # the device code objects embedded in the library name their target
+    lib = os.path.join(ROOT, "expert_ffn_moe_amd", "libmoe.so")
+    data = open(lib, "rb").read()
+    assert b"amdgcn-amd-amdhsa--gfx950" in data
+
+
+def test_status_strings(moe):
+    assert moe.status_str(0) == "ok"
+    assert "workspace" in moe.status_str(3)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=0), 1), (dict(k=9, E=8), 1), (dict(H=-1), 1), (dict(E=2000), 2), (dict(k=33, E=64), 2),
+    (dict(H=100), 2), (dict(I=96), 2), (dict(renormalize=2), 1),
+])
+def test_problem_check(moe, kw, status):
+    base = dict(T=64, H=128, E=8, k=2, I=128, capacity=0, renormalize=1, dtype="bf16")
+    base.update(kw)
+    assert moe.Problem(**base).check() == status
+
+
+def test_problem_check_dtype_pairs(moe):
+    p = moe.Problem(64, 128, 8, 2, 128)
+    c = p.c()
+    c.w_dtype = 0  # bf16 activations with fp32 weights: not handled
+    assert moe.lib.moe_problem_check(ctypes.byref(c)) == moe.MOE_ERR_UNSUPPORTED
+    c.w_dtype = 7
+    assert moe.lib.moe_problem_check(ctypes.byref(c)) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib.moe_problem_check(None) == moe.MOE_ERR_INVALID_ARG
+    # fp32 accepts multiples of 8
+    assert moe.Problem(64, 136, 8, 2, 24, dtype="f32").check() == 0
+
+
+def test_workspace_and_packed_sizes(moe):
+    p = moe.Problem(T=4096, H=2048, E=128, k=8, I=768)
+    assert p.workspace_bytes(moe.OP_ROUTE) == 0  # no cap: routing needs no scratch
+    assert p.workspace_bytes(moe.OP_COMBINE) == 0
+    assert p.workspace_bytes(moe.OP_DISPATCH) > 0
+    ffn = p.workspace_bytes(moe.OP_FFN)
+    assert ffn >= 4096 * 8 * 768 * 2  # the intermediate activation
+    assert p.workspace_bytes(moe.OP_LAYER) >= 2 * 4096 * 8 * 2048 * 2 + ffn
+    capped = moe.Problem(T=4096, H=2048, E=128, k=8, I=768, capacity=1024)
+    assert capped.workspace_bytes(moe.OP_ROUTE) >= 4096 * 8 * 4
+    assert p.packed_bytes(moe.W_GATE_UP) == 2 * 128 * 2048 * 768 * 2
+    assert p.packed_bytes(moe.W_DOWN) == 128 * 2048 * 768 * 2
+    bad = moe.Problem(T=0, H=2048, E=128, k=8, I=768)
+    assert bad.workspace_bytes(moe.OP_LAYER) == 0 and bad.packed_bytes(0) == 0
+
+
+def test_calls_reject_bad_arguments_before_touching_the_device(moe):
+    # NULL pointers and a missing workspace are refused on the host
+    p = moe.Problem(T=64, H=128, E=8, k=2, I=128, capacity=4)
+    c = p.c()
+    st = moe.lib.moe_route(ctypes.byref(c), None, None, None, None, None, 0, None)
+    assert st == moe.MOE_ERR_INVALID_ARG
+    fake = ctypes.c_void_p(256)
+    st = moe.lib.moe_route(ctypes.byref(c), fake, fake, fake, fake, None, 0, None)
+    assert st == moe.MOE_ERR_WORKSPACE
+    st = moe.lib.moe_combine(ctypes.byref(c), ctypes.c_void_p(8), fake, fake, fake, None)
+    assert st == moe.MOE_ERR_INVALID_ARG  # misaligned yp
+    bad = moe.Problem(T=64, H=100, E=8, k=2, I=128).c()
+    st = moe.lib.moe_layer(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, None, None,
+                           None, None, None, None, 0, None)
+    assert st == moe.MOE_ERR_UNSUPPORTED
