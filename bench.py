@@ -1,0 +1,220 @@
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic tokens:
+  moe_route -> moe_dispatch -> moe_expert_gate_up -> moe_expert_down -> moe_combine
+(capacity selection runs inside moe_route when the workload has a cap).  Inputs and the
+packed expert weights are resident in HBM before timing starts.
+
+Prints one JSON line: whole-step throughput in tokens/s, the roofline of the dominant
+kernel (per-launch algorithmic bytes or flops over its HIP-event-timed duration on the
+launch stream), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/sec on 1 MI355X; % bf16 MFMA peak (GEMM), % HBM peak (dispatch)"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
+PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA bf16; fp32 vector
+DEFAULT_WORKLOAD = "qwen3_30b_a3b"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def algorithmic(wl, N, E_hit):
+    """Per-launch algorithmic HBM bytes and flops of each stage (decimal units)."""
+    b = 2 if wl.dtype == "bf16" else 4
+    T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
+    return {
+        "route": dict(bytes=T * E * 4 + T * k * 9, flops=0),
+        "dispatch": dict(bytes=T * k * 5 + T * H * b + N * H * b + N * 8 + E * 8, flops=0),
+        "gate_up": dict(bytes=E_hit * 2 * H * I * b + N * H * b + N * I * b, flops=4 * N * H * I),
+        "down": dict(bytes=E_hit * I * H * b + N * I * b + N * H * b, flops=2 * N * H * I),
+        "combine": dict(bytes=N * H * b + T * k * 8 + T * H * b, flops=0),
+    }
+
+
+def roofline_of(stage, alg, sec, dtype):
+    a = alg[stage]
+    t_hbm = a["bytes"] / (PEAK_HBM_GBS * 1e9)
+    t_mfma = a["flops"] / (PEAK_TFLOPS[dtype] * 1e12) if a["flops"] else 0.0
+    if t_mfma > t_hbm:
+        ach = a["flops"] / sec / 1e12
+        return dict(bound="mfma" if dtype == "bf16" else "alu", achieved=round(ach, 2),
+                    peak=PEAK_TFLOPS[dtype], unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS[dtype], 4))
+    ach = a["bytes"] / sec / 1e9
+    return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                frac=round(ach / PEAK_HBM_GBS, 4))
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "expert_ffn_moe_amd", "csrc"))):
+        h.update(open(os.path.join(ROOT, "expert_ffn_moe_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, stage):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(PROFILES, f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sources") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, inp, target_s):
+    """The oracle (as it stands) on a bounded sample: routing, capacity and layout over all
+    T tokens, the FFN and combine over a sample of tokens; scaled to tokens/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    import torch
+
+    threads = min(16, len(os.sched_getaffinity(0)))
+    host = {n: (synth.bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy())
+            for n, t in inp.items()}
+    t0 = time.perf_counter()
+    ids, w = oracle.route(host["logits"], wl.k, wl.renormalize)
+    keep = oracle.capacity(ids, w, wl.E, wl.capacity)
+    lay = oracle.layout(ids, keep, wl.E)
+    t_route = time.perf_counter() - t0
+    rng = np.random.default_rng(0)
+
+    def ffn_for(tokens):
+        rows = lay["slot_to_row"][tokens].ravel()
+        rows = np.sort(rows[rows >= 0])
+        rexp = (np.searchsorted(lay["offsets"], rows, side="right") - 1).astype(np.int32)
+        xrows = host["x"][lay["row_token"][rows]]
+        t1 = time.perf_counter()
+        yp = oracle.ffn_rows(xrows, rexp, host["w_gate"], host["w_up"], host["w_down"], nthreads=threads)
+        pos = {int(r): i for i, r in enumerate(rows)}
+        s2r = np.array([[pos.get(int(r), -1) for r in lay["slot_to_row"][t]] for t in tokens], np.int32)
+        oracle.combine(np.arange(len(tokens), dtype=np.int32), w[tokens], s2r, yp)
+        return time.perf_counter() - t1
+
+    # calibrate on a few tokens, then size the sample to about target_s of CPU time
+    n0 = min(wl.T, 8)
+    t_small = ffn_for(rng.choice(wl.T, n0, replace=False))
+    per_tok = max(t_small / n0, 1e-6)
+    n = int(min(wl.T, max(n0, target_s / per_tok)))
+    tokens = rng.choice(wl.T, n, replace=False)
+    t_ffn = ffn_for(tokens)
+    total = t_route + t_ffn * wl.T / n
+    return dict(value=round(wl.T / total, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"routing+capacity+layout over all {wl.T} tokens ({t_route:.2f} s); FFN+combine "
+                       f"over {n} random tokens ({t_ffn:.2f} s), scaled to {wl.T} tokens")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import expert_ffn_moe_amd as moe
+    import synth
+
+    wl = synth.WORKLOADS[args.config]
+    p = moe.Problem.of(wl)
+    dev = "cuda"
+    inp = synth.make_inputs(wl, dev)
+    pgu, pd = moe.pack_weights(p, inp["w_gate"], inp["w_up"], inp["w_down"])
+    torch.cuda.synchronize()
+    tk = wl.T * wl.k
+    dt = p.torch_dtype
+    # every buffer allocated once, outside the timed region
+    ws = {op: moe.workspace(p, op, dev) for op in (moe.OP_ROUTE, moe.OP_DISPATCH, moe.OP_FFN)}
+    routing = (torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev),
+               torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev),
+               torch.empty(wl.T, wl.k, dtype=torch.uint8, device=dev))
+    disp = dict(counts=torch.empty(wl.E, dtype=torch.int32, device=dev),
+                offsets=torch.empty(wl.E + 1, dtype=torch.int32, device=dev),
+                row_token=torch.empty(tk, dtype=torch.int32, device=dev),
+                slot_to_row=torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev),
+                xp=torch.empty(tk, wl.H, dtype=dt, device=dev))
+    a = torch.empty(tk, wl.I, dtype=dt, device=dev)
+    yp = torch.empty(tk, wl.H, dtype=dt, device=dev)
+    y = torch.empty(wl.T, wl.H, dtype=dt, device=dev)
+    stages = ["route", "dispatch", "gate_up", "down", "combine"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        ids, w, keep = moe.route(p, inp["logits"], out=routing, ws=ws[moe.OP_ROUTE])
+        mark(1)
+        moe.dispatch(p, inp["x"], ids, keep if wl.capacity > 0 else None, out=disp, ws=ws[moe.OP_DISPATCH])
+        mark(2)
+        moe.expert_gate_up(p, disp["xp"], disp["offsets"], pgu, out=a, ws=ws[moe.OP_FFN])
+        mark(3)
+        moe.expert_down(p, a, disp["offsets"], pd, out=yp, ws=ws[moe.OP_FFN])
+        mark(4)
+        moe.combine(p, yp, w, disp["slot_to_row"], out=y)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec = (t1 - t0) / args.steps
+    stage_ms = {s: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
+                for j, s in enumerate(stages)}
+
+    N = int(disp["offsets"][-1].item())
+    E_hit = int((disp["counts"] > 0).sum().item())
+    alg = algorithmic(wl, N, E_hit)
+    dom = max(("gate_up", "down", "dispatch", "combine", "route"), key=lambda s: stage_ms[s])
+    roof = roofline_of(dom, alg, stage_ms[dom] / 1e3, wl.dtype)
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(wl.name, dom)
+    per_stage = {s: dict(us=round(stage_ms[s] * 1e3, 2),
+                         **{k: v for k, v in roofline_of(s, alg, stage_ms[s] / 1e3, wl.dtype).items()
+                            if k in ("bound", "achieved", "unit", "frac")}) for s in stages}
+    out = {
+        "metric": METRIC, "value": round(wl.T / sec, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded; routing logits and weights drawn per the workload recipe)",
+        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
+                   "capacity": wl.capacity, "N_kept": N, "experts_hit": E_hit},
+        "roofline": roof, "stages": per_stage,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
