@@ -8,13 +8,15 @@
 //   down   : yp[r] = a[r] Wd[e]
 //
 // Two kernel shapes, chosen from the problem shape:
-//  * prefill (many rows per expert): 128-row M tiles listed in a device-built tile table;
-//    the activation tile goes through LDS (shared by the 8 wavefronts of the block) and
-//    each wavefront streams its own weight panels straight from HBM into registers in
+//  * prefill (many rows per expert): persistent, XCD-aware grouped GEMM over 128-row M
+//    tiles; the activation tile goes through LDS (shared by the 4 wavefronts of a block)
+//    and each wavefront streams its own weight operands straight into registers in
 //    matrix-core operand order (the packed layout makes each operand a contiguous 1 KiB).
 //    v_mfma_f32_32x32x16_bf16.
 //  * decode (a few rows per expert): a weight-streaming kernel; one wavefront per
 //    32/64-column panel of one expert, 16-row M steps, v_mfma_f32_16x16x32_bf16.
+#include <algorithm>
+
 #include "bf16.h"
 #include "moe_internal.h"
 #include "wave.h"
@@ -35,168 +37,202 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 constexpr int kOperandElems = 512;  // one packed 32x16 (or 16x32) operand block
 
 // ------------------------------------------------------------------------------------
-// Tile table: expert e with c rows gets ceil(c / 128) consecutive tiles.
+// Prefill grouped GEMM: persistent, one block of 4 wavefronts per CU.
+//
+// Work item = (M tile of 128 rows of one expert, N group).  Wavefront w of the block
+// computes 128 rows x 4 operand columns (4 x 32 = 128 GEMM columns):
+//   GATE_UP: gate and up columns of 64 outputs of `a` -> block covers 256 columns of a
+//   DOWN   : 128 columns of yp                          -> block covers 512 columns of yp
+// 16 accumulators of 32x32 (256 fp32 registers per lane, held in AGPRs).
+//
+// K runs in stages of 64 (4 MFMA k-steps).  The 128x64 activation stage goes through LDS
+// (double-buffered, matrix-core operand order, shared by the 4 wavefronts); each
+// wavefront's weight operands come straight from memory into registers, one stage ahead.
+//
+// Scheduling: every block first turns `offsets` into per-expert M-tile starts (LDS).  The
+// M tiles are split into 8 contiguous ranges, one per XCD (workgroups are dispatched to
+// XCDs round-robin, so block b runs on XCD b % 8); the blocks of an XCD take its work
+// items in turn.  Items of one expert therefore run together on one XCD, and the weight
+// and activation bytes they share are served by that XCD's L2.
 // ------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets,
-                                                          int E, int32_t* __restrict__ count,
-                                                          int32_t* __restrict__ tile_expert,
-                                                          int32_t* __restrict__ tile_row0) {
-  __shared__ int wsum[16];
-  const int e = threadIdx.x, wave = e >> 6, lane = e & 63;
-  int n = 0, o = 0;
-  if (e < E) {
-    o = offsets[e];
-    n = div_up(offsets[e + 1] - o, kPrefillBM);
-  }
-  const int inc = wave_inclusive_scan(n);
-  if (lane == 63) wsum[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-  const int start = base + inc - n;
-  for (int m = 0; m < n; ++m) {
-    tile_expert[start + m] = e;
-    tile_row0[start + m] = o + m * kPrefillBM;
-  }
-  if (e == E - 1) count[0] = base + inc;
-}
+constexpr int kXcds = 8;
+constexpr int kMaxExperts = 1024;
 
-// ------------------------------------------------------------------------------------
-// Prefill grouped GEMM.  Block = 8 wavefronts, tile = 128 rows x 8 panels.
-//   GATE_UP: panel = 32 output columns of `a` = one gate and one up operand column.
-//   DOWN   : panel = 64 output columns of yp = two operand columns.
-// K steps of 64 (4 MFMA k-steps); LDS double-buffers the activation tile.
-// ------------------------------------------------------------------------------------
 template <bool GATE_UP>
-__global__ __launch_bounds__(512) void prefill_kernel(
-    const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ tile_count, const int32_t* __restrict__ tile_expert,
-    const int32_t* __restrict__ tile_row0, const uint16_t* __restrict__ Bp,
-    uint16_t* __restrict__ out, int K, int Nout, int ntn) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E,
+                    const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout) {
   __shared__ uint4 lds_a[2][16 * 64];  // [buf][(m32 * 4 + k16) * 64 + lane]
+  __shared__ int s_start[kMaxExperts + 1];
+  __shared__ int s_wsum[4];
 
-  // linear block index -> (M tile, N panel group), N fastest so that the blocks sharing
-  // an activation tile run together
-  const int mt = blockIdx.x / ntn;
-  const int nt = blockIdx.x - mt * ntn;
-  if (mt >= tile_count[0]) return;  // block-uniform
-  const int e = tile_expert[mt];
-  const int row0 = tile_row0[mt];
-  const int rows = min(kPrefillBM, offsets[e + 1] - row0);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+
+  // ---- per-expert M-tile starts (exclusive scan of ceil(count / 128))
+  {
+    const int per = div_up(E, 256);
+    const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+    int sum = 0;
+    for (int e = e0; e < e1; ++e) sum += div_up(offsets[e + 1] - offsets[e], kPrefillBM);
+    const int inc = wave_inclusive_scan(sum);
+    if (lane == 63) s_wsum[wave] = inc;
+    __syncthreads();
+    int base = inc - sum;
+    for (int w = 0; w < wave; ++w) base += s_wsum[w];
+    for (int e = e0; e < e1; ++e) {
+      s_start[e] = base;
+      base += div_up(offsets[e + 1] - offsets[e], kPrefillBM);
+    }
+    if (tid == 255) s_start[E] = base;
+    __syncthreads();
+  }
+  const int total_mt = s_start[E];
   const int nk16 = K / 16;
   const int nf32 = Nout / 32;
+  const int ntn = GATE_UP ? div_up(nf32, 8) : div_up(nf32, 16);
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int nslots = gridDim.x / kXcds;
+  const int mt_lo = (int)((int64_t)total_mt * xcd / kXcds);
+  const int mt_hi = (int)((int64_t)total_mt * (xcd + 1) / kXcds);
+  const int items = (mt_hi - mt_lo) * ntn;
+  const int nst = K / 64;
 
-  // this wavefront's two operand columns (clamped when the panel lies past Nout)
-  int col0;
-  bool active;
-  const uint16_t* b0;
-  const uint16_t* b1;
-  if (GATE_UP) {
-    int af = nt * 8 + wave;
-    active = af < nf32;
-    af = min(af, nf32 - 1);
-    col0 = af * 32;
-    b0 = Bp + (size_t)(e * nf32 + af) * 2 * nk16 * kOperandElems;
-    b1 = b0 + (size_t)nk16 * kOperandElems;
-  } else {
-    int nf = nt * 16 + 2 * wave;
-    active = nf < nf32;
-    nf = min(nf, nf32 - 2);
-    col0 = nf * 32;
-    b0 = Bp + (size_t)(e * nf32 + nf) * nk16 * kOperandElems;
-    b1 = b0 + (size_t)nk16 * kOperandElems;
-  }
-  b0 += lane * 8;
-  b1 += lane * 8;
+  for (int item = slot; item < items; item += nslots) {
+    const int mt = mt_lo + item / ntn;
+    const int nt = item - (item / ntn) * ntn;
+    // expert of tile mt: the largest e with s_start[e] <= mt
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_start[mid] <= mt) lo = mid; else hi = mid;
+    }
+    const int e = lo;
+    const int row0 = offsets[e] + (mt - s_start[e]) * kPrefillBM;
+    const int rows = min(kPrefillBM, offsets[e + 1] - row0);
 
-  // activation tile loader: 1024 16-byte pieces, two per thread
-  const uint16_t* ag[2];
-  int lds_slot[2];
+    // this wavefront's 4 operand columns
+    const uint16_t* bs[4];
+    int fcol[4];
+    bool act[4];
+    const size_t panel = (size_t)nk16 * kOperandElems;
+    if (GATE_UP) {
+      int af0 = (nt * 4 + wave) * 2;  // two 32-column groups of `a`
+      act[0] = act[1] = act[2] = act[3] = af0 < nf32;
+      af0 = min(af0, nf32 - 2);
+      const uint16_t* g0 = Bp + (size_t)(e * nf32 + af0) * 2 * panel;
+      bs[0] = g0;              // gate, columns af0
+      bs[1] = g0 + 2 * panel;  // gate, columns af0 + 1
+      bs[2] = g0 + panel;      // up,   columns af0
+      bs[3] = g0 + 3 * panel;  // up,   columns af0 + 1
+      fcol[0] = fcol[2] = af0 * 32;
+      fcol[1] = fcol[3] = af0 * 32 + 32;
+    } else {
+      const int nf0 = (nt * 4 + wave) * 4;
 #pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int idx = threadIdx.x + 512 * p;
-    const int r = idx >> 3, q = idx & 7;
-    ag[p] = A + (size_t)(row0 + min(r, rows - 1)) * K + q * 8;
-    lds_slot[p] = ((r >> 5) * 4 + (q >> 1)) * 64 + (r & 31) + 32 * (q & 1);
-  }
-
-  f32x16_t acc0[4], acc1[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    acc0[m] = f32x16_t{};
-    acc1[m] = f32x16_t{};
-  }
-
-  const int nkt = K / 64;
-  uint4 areg[2], bcur[4][2], bnext[4][2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) areg[p] = *(const uint4*)(ag[p]);
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    bcur[kk][0] = *(const uint4*)(b0 + (size_t)kk * kOperandElems);
-    bcur[kk][1] = *(const uint4*)(b1 + (size_t)kk * kOperandElems);
-  }
-#pragma unroll
-  for (int p = 0; p < 2; ++p) lds_a[0][lds_slot[p]] = areg[p];
-  __syncthreads();
-
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-#pragma unroll
-      for (int p = 0; p < 2; ++p) areg[p] = *(const uint4*)(ag[p] + (size_t)(kt + 1) * 64);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const size_t o = (size_t)((kt + 1) * 4 + kk) * kOperandElems;
-        bnext[kk][0] = *(const uint4*)(b0 + o);
-        bnext[kk][1] = *(const uint4*)(b1 + o);
+      for (int c = 0; c < 4; ++c) {
+        act[c] = nf0 + c < nf32;
+        const int f = min(nf0 + c, nf32 - 1);
+        bs[c] = Bp + (size_t)(e * nf32 + f) * panel;
+        fcol[c] = f * 32;
       }
     }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8_t a[4];
+    for (int c = 0; c < 4; ++c) bs[c] += lane * 8;
+
+    // activation stage loader: wavefront w fills the 4 operand fragments of rows
+    // 32w .. 32w+31 (one per k-step); lane L of the p-th load takes row 32w + L%32,
+    // k-offset 16p + 8*(L/32), so every LDS write is one contiguous 1 KiB fragment.
+    const uint16_t* ag[4];
+    int lslot[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(lds_a[cur][(m * 4 + kk) * 64 + lane]);
-      const bf16x8_t bb0 = as_bf16x8(bcur[kk][0]);
-      const bf16x8_t bb1 = as_bf16x8(bcur[kk][1]);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        acc0[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bb0, acc0[m], 0, 0, 0);
-        acc1[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bb1, acc1[m], 0, 0, 0);
-      }
+    for (int p = 0; p < 4; ++p) {
+      const int r = wave * 32 + (lane & 31);
+      ag[p] = A + (size_t)(row0 + min(r, rows - 1)) * K + p * 16 + (lane >> 5) * 8;
+      lslot[p] = (wave * 4 + p) * 64 + lane;
     }
-    if (more) {
+
+    f32x16_t acc[4][4];
 #pragma unroll
-      for (int p = 0; p < 2; ++p) lds_a[cur ^ 1][lds_slot[p]] = areg[p];
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[m][c] = f32x16_t{};
+
+    // b[kk][c]: operand column c of k-step kk of the current stage.  Each k-step's
+    // registers are refilled with the next stage's operands as soon as its MFMAs are
+    // issued, so a load has a whole stage (16 MFMAs x 4 k-steps) to land.
+    uint4 areg[4], b[4][4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) areg[p] = *(const uint4*)(ag[p]);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) b[kk][c] = *(const uint4*)(bs[c] + (size_t)kk * kOperandElems);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) lds_a[0][lslot[p]] = areg[p];
     __syncthreads();
-    if (more) {
+
+    for (int st = 0; st < nst; ++st) {
+      const int cur = st & 1;
+      // Next stage's operands.  The loads are unconditional (the last stage reloads
+      // itself, into registers and a buffer nobody reads) so that the compiler cannot
+      // merge the load and the LDS store behind one branch and wait on the load at once.
+      const int sn = min(st + 1, nst - 1);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) areg[p] = *(const uint4*)(ag[p] + (size_t)sn * 64);
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8_t a[4], an[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(lds_a[cur][(m * 4 + 0) * 64 + lane]);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bcur[kk][0] = bnext[kk][0];
-        bcur[kk][1] = bnext[kk][1];
+        // the next k-step's activation fragments are read before this k-step's MFMAs
+        if (kk < 3) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) an[m] = as_bf16x8(lds_a[cur][(m * 4 + kk + 1) * 64 + lane]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8_t bv = as_bf16x8(b[kk][c]);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[m][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv, acc[m][c], 0, 0, 0);
+        }
+        const size_t o = (size_t)(sn * 4 + kk) * kOperandElems;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) b[kk][c] = *(const uint4*)(bs[c] + o);
+        if (kk < 3) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) a[m] = an[m];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) lds_a[cur ^ 1][lslot[p]] = areg[p];
+      __syncthreads();
     }
-  }
 
-  if (!active) return;
-  // 32x32 accumulator layout: element i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-  // column l%32.
-  const int c = col0 + (lane & 31);
+    // 32x32 accumulator layout: element i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
+    // column l%32.
+    const int lc = lane & 31;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = m * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      if (r < rows) {
-        uint16_t* o = out + (size_t)(row0 + r) * Nout;
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+        if (r >= rows) continue;
+        uint16_t* o = out + (size_t)(row0 + r) * Nout + lc;
         if (GATE_UP) {
-          o[c] = to_bf16(silu_mul(acc0[m][i], acc1[m][i]));
+          if (act[0]) {
+            o[fcol[0]] = to_bf16(silu_mul(acc[m][0][i], acc[m][2][i]));
+            o[fcol[1]] = to_bf16(silu_mul(acc[m][1][i], acc[m][3][i]));
+          }
         } else {
-          o[c] = to_bf16(acc0[m][i]);
-          o[c + 32] = to_bf16(acc1[m][i]);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (act[c]) o[fcol[c]] = to_bf16(acc[m][c][i]);
         }
       }
     }
@@ -281,41 +317,48 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 // Decode shape: few rows per expert on average.
 bool ffn_use_decode(const moe_problem& p) { return (int64_t)p.T * p.k <= (int64_t)24 * p.E; }
 
-hipError_t launch_tile_table(const moe_problem& p, const int32_t* offsets, TileTable tt,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, s, offsets, p.E, tt.tile_count,
-                     tt.tile_expert, tt.tile_row0);
-  return hipGetLastError();
+namespace {
+int cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
 }
+int persistent_grid() { return std::max(kXcds, cu_count() / kXcds * kXcds); }
+}  // namespace
 
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32_t* offsets,
-                               const void* packed_gu, void* a, TileTable tt, hipStream_t s) {
-  const int nf32 = p.I / 32;
+                               const void* packed_gu, void* a, hipStream_t s) {
   if (ffn_use_decode(p)) {
+    const int nf32 = p.I / 32;
     hipLaunchKernelGGL(decode_kernel<true>, dim3(div_up(nf32, 4), p.E), dim3(256), 0, s,
                        (const uint16_t*)xp, offsets, (const uint16_t*)packed_gu, (uint16_t*)a,
                        p.H, p.I);
   } else {
-    const int ntn = div_up(nf32, 8);
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(ntn * tt.max_tiles), dim3(512), 0, s,
-                       (const uint16_t*)xp, offsets, tt.tile_count, tt.tile_expert,
-                       tt.tile_row0, (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I, ntn);
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(persistent_grid()), dim3(256), 0, s,
+                       (const uint16_t*)xp, offsets, p.E, (const uint16_t*)packed_gu,
+                       (uint16_t*)a, p.H, p.I);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, TileTable tt, hipStream_t s) {
-  const int nf32 = p.H / 32;
+                            const void* packed_d, void* yp, hipStream_t s) {
   if (ffn_use_decode(p)) {
+    const int nf32 = p.H / 32;
     hipLaunchKernelGGL(decode_kernel<false>, dim3(div_up(nf32 / 2, 4), p.E), dim3(256), 0, s,
                        (const uint16_t*)a, offsets, (const uint16_t*)packed_d, (uint16_t*)yp,
                        p.I, p.H);
   } else {
-    const int ntn = div_up(nf32, 16);
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(ntn * tt.max_tiles), dim3(512), 0, s,
-                       (const uint16_t*)a, offsets, tt.tile_count, tt.tile_expert,
-                       tt.tile_row0, (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H, ntn);
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(persistent_grid()), dim3(256), 0, s,
+                       (const uint16_t*)a, offsets, p.E, (const uint16_t*)packed_d,
+                       (uint16_t*)yp, p.I, p.H);
   }
   return hipGetLastError();
 }

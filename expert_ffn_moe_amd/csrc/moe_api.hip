@@ -20,15 +20,6 @@ RankScratch carve_rank(Carve& c, const moe_problem& p, bool with_capacity) {
   return r;
 }
 
-TileTable carve_tiles(Carve& c, const moe_problem& p) {
-  TileTable t{};
-  t.max_tiles = div_up(p.T * p.k, kPrefillBM) + p.E;
-  t.tile_count = c.take<int32_t>(1);
-  t.tile_expert = c.take<int32_t>(t.max_tiles);
-  t.tile_row0 = c.take<int32_t>(t.max_tiles);
-  return t;
-}
-
 }  // namespace moe
 
 using namespace moe;
@@ -41,15 +32,14 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Workspace of the FFN: the intermediate activation plus the tile table.
+// Workspace of the FFN: the intermediate activation (moe_expert_ffn and moe_layer only;
+// the split calls take it as an argument and need no workspace).
 struct FfnScratch {
   void* a;
-  TileTable tt;
 };
 FfnScratch carve_ffn(Carve& c, const moe_problem& p) {
   FfnScratch f{};
   f.a = c.take<char>((size_t)p.T * p.k * p.I * elem_bytes(p.act_dtype));
-  f.tt = carve_tiles(c, p);
   return f;
 }
 
@@ -141,30 +131,20 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
 }
 
 hipError_t run_gate_up(const moe_problem& p, const void* xp, const int32_t* offsets,
-                       const void* pgu, void* a, const TileTable& tt, bool need_table,
-                       hipStream_t s) {
+                       const void* pgu, void* a, hipStream_t s) {
   if (p.act_dtype == MOE_F32) {
     const size_t n = (size_t)p.E * p.H * p.I;
     return launch_gate_up_f32(p, (const float*)xp, offsets, (const float*)pgu,
                               (const float*)pgu + n, (float*)a, s);
   }
-  if (need_table && !ffn_use_decode(p)) {
-    hipError_t err = launch_tile_table(p, offsets, tt, s);
-    if (err != hipSuccess) return err;
-  }
-  return launch_gate_up_bf16(p, xp, offsets, pgu, a, tt, s);
+  return launch_gate_up_bf16(p, xp, offsets, pgu, a, s);
 }
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
-                    const void* pd, void* yp, const TileTable& tt, bool need_table,
-                    hipStream_t s) {
+                    const void* pd, void* yp, hipStream_t s) {
   if (p.act_dtype == MOE_F32)
     return launch_down_f32(p, (const float*)a, offsets, (const float*)pd, (float*)yp, s);
-  if (need_table && !ffn_use_decode(p)) {
-    hipError_t err = launch_tile_table(p, offsets, tt, s);
-    if (err != hipSuccess) return err;
-  }
-  return launch_down_bf16(p, a, offsets, pd, yp, tt, s);
+  return launch_down_bf16(p, a, offsets, pd, yp, s);
 }
 
 }  // namespace
@@ -257,11 +237,9 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
   if (st != MOE_OK) return st;
   if (!xp || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
   if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
-  if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
-  Carve c(ws);
-  FfnScratch f = carve_ffn(c, *p);
-  return status_of(run_gate_up(*p, xp, offsets, packed_gate_up, a, f.tt, true,
-                               as_stream(stream)));
+  (void)ws;
+  (void)ws_bytes;
+  return status_of(run_gate_up(*p, xp, offsets, packed_gate_up, a, as_stream(stream)));
 }
 
 int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
@@ -271,10 +249,9 @@ int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
   if (st != MOE_OK) return st;
   if (!a || !offsets || !packed_down || !yp) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(packed_down) || !aligned16(yp)) return MOE_ERR_INVALID_ARG;
-  if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
-  Carve c(ws);
-  FfnScratch f = carve_ffn(c, *p);
-  return status_of(run_down(*p, a, offsets, packed_down, yp, f.tt, true, as_stream(stream)));
+  (void)ws;
+  (void)ws_bytes;
+  return status_of(run_down(*p, a, offsets, packed_down, yp, as_stream(stream)));
 }
 
 int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
@@ -290,8 +267,8 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   Carve c(ws);
   FfnScratch f = carve_ffn(c, *p);
   hipStream_t s = as_stream(stream);
-  hipError_t err = run_gate_up(*p, xp, offsets, packed_gate_up, f.a, f.tt, true, s);
-  if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, f.tt, false, s);
+  hipError_t err = run_gate_up(*p, xp, offsets, packed_gate_up, f.a, s);
+  if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, s);
   return status_of(err);
 }
 
@@ -329,10 +306,8 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if (err == hipSuccess)
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
                        row_token, slot_to_row, L.xp, L.rank, s);
-  if (err == hipSuccess)
-    err = run_gate_up(*p, L.xp, offsets, packed_gate_up, L.ffn.a, L.ffn.tt, true, s);
-  if (err == hipSuccess)
-    err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, L.ffn.tt, false, s);
+  if (err == hipSuccess) err = run_gate_up(*p, L.xp, offsets, packed_gate_up, L.ffn.a, s);
+  if (err == hipSuccess) err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, s);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, y, s);
   return status_of(err);
 }

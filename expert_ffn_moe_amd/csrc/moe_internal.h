@@ -40,16 +40,6 @@ struct RankScratch {
 };
 RankScratch carve_rank(Carve& c, const moe_problem& p, bool with_capacity);
 
-// Tile table of the prefill grouped GEMM: tile i covers rows [row0, row0 + 128) of
-// expert tile_expert[i]; tile_count[0] tiles in total.
-struct TileTable {
-  int32_t* tile_count;   // [1]
-  int32_t* tile_expert;  // [max_tiles]
-  int32_t* tile_row0;    // [max_tiles]
-  int max_tiles;
-};
-TileTable carve_tiles(Carve& c, const moe_problem& p);
-
 // ---- route.hip
 hipError_t launch_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
                         uint8_t* keep, hipStream_t s);
@@ -85,12 +75,10 @@ hipError_t launch_pack(const moe_problem& p, const void* wg, const void* wu, con
 
 // ---- ffn_bf16.hip / ffn_f32.hip
 bool ffn_use_decode(const moe_problem& p);
-hipError_t launch_tile_table(const moe_problem& p, const int32_t* offsets, TileTable tt,
-                             hipStream_t s);
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32_t* offsets,
-                               const void* packed_gu, void* a, TileTable tt, hipStream_t s);
+                               const void* packed_gu, void* a, hipStream_t s);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, TileTable tt, hipStream_t s);
+                            const void* packed_d, void* yp, hipStream_t s);
 hipError_t launch_gate_up_f32(const moe_problem& p, const float* xp, const int32_t* offsets,
                               const float* wg, const float* wu, float* a, hipStream_t s);
 hipError_t launch_down_f32(const moe_problem& p, const float* a, const int32_t* offsets,

@@ -76,7 +76,7 @@ typedef struct {
 typedef enum {
   MOE_OP_ROUTE = 0,
   MOE_OP_DISPATCH = 1,
-  MOE_OP_FFN = 2, /* moe_expert_ffn, moe_expert_gate_up and moe_expert_down */
+  MOE_OP_FFN = 2, /* moe_expert_ffn (moe_expert_gate_up / moe_expert_down need none) */
   MOE_OP_COMBINE = 3,
   MOE_OP_LAYER = 4
 } moe_op;
@@ -165,7 +165,8 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
  *
  *   xp [T*k, H], a [T*k, I], yp [T*k, H] (act dtype); offsets [E+1] i32;
  *   packed_gate_up / packed_down from moe_pack_weights.
- * moe_expert_ffn keeps `a` in the workspace; the two halves are also callable alone.
+ * moe_expert_ffn keeps `a` in the workspace; the two halves are also callable alone and
+ * need no workspace (their ws / ws_bytes arguments are ignored and may be NULL / 0).
  * --------------------------------------------------------------------------------- */
 int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
                    const void* packed_gate_up, const void* packed_down, void* yp, void* ws,
