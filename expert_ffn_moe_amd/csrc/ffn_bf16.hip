@@ -39,15 +39,19 @@ constexpr int kOperandElems = 512;  // one packed 32x16 (or 16x32) operand block
 // ------------------------------------------------------------------------------------
 // Prefill grouped GEMM: persistent, one block of 4 wavefronts per CU.
 //
-// Work item = (M tile of 128 rows of one expert, N group).  Wavefront w of the block
-// computes 128 rows x 4 operand columns (4 x 32 = 128 GEMM columns):
-//   GATE_UP: gate and up columns of 64 outputs of `a` -> block covers 256 columns of a
-//   DOWN   : 128 columns of yp                          -> block covers 512 columns of yp
-// 16 accumulators of 32x32 (256 fp32 registers per lane, held in AGPRs).
+// Work item = (M tile of up to 256 rows of one expert, N group).  Wavefront w computes
+// all rows of the tile for 2 operand columns (64 GEMM columns):
+//   GATE_UP: the gate and the up column of 32 outputs of `a` -> block: 128 columns of a
+//   DOWN   : 64 columns of yp                               -> block: 256 columns of yp
+// 8 x 2 accumulators of 32x32 (256 fp32 per lane, in AGPRs); 32-row fragments past the
+// expert's last row are skipped, so a ragged tile costs at most 31 idle rows.
 //
-// K runs in stages of 64 (4 MFMA k-steps).  The 128x64 activation stage goes through LDS
-// (double-buffered, matrix-core operand order, shared by the 4 wavefronts); each
-// wavefront's weight operands come straight from memory into registers, one stage ahead.
+// K runs in k-steps of 16 (one MFMA) grouped in stages of two.  Weight operands come
+// straight from memory into a ring of 8 k-steps of registers (refilled as soon as a
+// k-step's MFMAs are issued).  The 256x32 activation stage goes through LDS (double
+// buffer, operand order, one contiguous 1 KiB fragment per wavefront store) and is
+// loaded into registers 3 stages ahead.  Every wait therefore covers loads issued at
+// least 3 stages earlier, although vector-memory counters complete in issue order.
 //
 // Scheduling: every block first turns `offsets` into per-expert M-tile starts (LDS).  The
 // M tiles are split into 8 contiguous ranges, one per XCD (workgroups are dispatched to
@@ -57,19 +61,150 @@ constexpr int kOperandElems = 512;  // one packed 32x16 (or 16x32) operand block
 // ------------------------------------------------------------------------------------
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
+constexpr int kRing = 8;  // weight ring depth in k-steps
+
+struct TileArgs {
+  const uint16_t* A;     // activation rows of the tile (row0), row stride K
+  const uint16_t* b0;    // first operand column of this wavefront (lane offset applied)
+  const uint16_t* b1;    // second operand column
+  uint16_t* out;         // output row row0, column col0 (row stride Nout)
+  int K, Nout, rows, wave, lane, act;
+};
+
+// One step of the k loop: MFMAs of k-step (2 * stage + KK) from LDS buffer BUF and ring
+// slot SLOT, then the ring slot is refilled with the operands KRING k-steps ahead.
+template <int NM, int BUF, int KK, int SLOT>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[8][2], uint4 (&bring)[kRing][2],
+                                      const uint4 (*lds)[16 * 64], const TileArgs& t,
+                                      int j_next) {
+  bf16x8_t a[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) a[m] = as_bf16x8(lds[BUF][(m * 2 + KK) * 64 + t.lane]);
+  const bf16x8_t bv0 = as_bf16x8(bring[SLOT][0]);
+  const bf16x8_t bv1 = as_bf16x8(bring[SLOT][1]);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv0, acc[m][0], 0, 0, 0);
+    acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv1, acc[m][1], 0, 0, 0);
+  }
+  const size_t o = (size_t)j_next * kOperandElems;
+  bring[SLOT][0] = *(const uint4*)(t.b0 + o);
+  bring[SLOT][1] = *(const uint4*)(t.b1 + o);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage (two k-steps) with stage index s; U = s mod 4 picks registers and buffers.
+template <int NM, int U>
+__device__ __forceinline__ void kstage(f32x16_t (&acc)[8][2], uint4 (&bring)[kRing][2],
+                                       uint4 (&aset)[4][4], uint4 (*lds)[16 * 64],
+                                       const uint16_t* const (&ag)[4], const int (&lslot)[4],
+                                       bool (&aload)[4], const TileArgs& t, int s, int nst,
+                                       int nk16) {
+  const int sa = min(s + 3, nst - 1);
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    if (aload[p]) aset[(U + 3) & 3][p] = *(const uint4*)(ag[p] + (size_t)sa * 32);
+  __builtin_amdgcn_sched_barrier(0);
+  kstep<NM, U & 1, 0, (2 * U) & 7>(acc, bring, lds, t, min(2 * s + kRing, nk16 - 1));
+  kstep<NM, U & 1, 1, (2 * U + 1) & 7>(acc, bring, lds, t, min(2 * s + 1 + kRing, nk16 - 1));
+#pragma unroll
+  for (int p = 0; p < 4; ++p) lds[(U + 1) & 1][lslot[p]] = aset[(U + 1) & 3][p];
+  __syncthreads();
+}
+
+// A whole work item with NM live 32-row fragments (NM = 2, 4, 6 or 8).
+template <bool GATE_UP, int NM>
+__device__ __forceinline__ void prefill_tile(const TileArgs& t, uint4 (*lds)[16 * 64]) {
+  const int nk16 = t.K / 16, nst = t.K / 32;
+  const int lane = t.lane, wave = t.wave;
+  // activation loader: wavefront w fills fragments (m32 = 2w + p/2, k16 = p%2); lane L
+  // takes row 32*m32 + L%32, k-offset 16*(p%2) + 8*(L/32): one contiguous LDS store each
+  const uint16_t* ag[4];
+  int lslot[4];
+  bool aload[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int mf = 2 * wave + (p >> 1), kf = p & 1;
+    const int r = mf * 32 + (lane & 31);
+    ag[p] = t.A + (size_t)min(r, t.rows - 1) * t.K + kf * 16 + (lane >> 5) * 8;
+    lslot[p] = (mf * 2 + kf) * 64 + lane;
+    aload[p] = mf < NM;
+  }
+  f32x16_t acc[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = f32x16_t{};
+  uint4 aset[4][4];
+  uint4 bring[kRing][2];
+#pragma unroll
+  for (int u = 0; u < 3; ++u) {
+    const int st = min(u, nst - 1);
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      aset[u][p] = aload[p] ? *(const uint4*)(ag[p] + (size_t)st * 32) : uint4{0, 0, 0, 0};
+  }
+  aset[3][0] = aset[3][1] = aset[3][2] = aset[3][3] = uint4{0, 0, 0, 0};
+#pragma unroll
+  for (int q = 0; q < kRing; ++q) {
+    const size_t o = (size_t)min(q, nk16 - 1) * kOperandElems;
+    bring[q][0] = *(const uint4*)(t.b0 + o);
+    bring[q][1] = *(const uint4*)(t.b1 + o);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p) lds[0][lslot[p]] = aset[0][p];
+  __syncthreads();
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    kstage<NM, 0>(acc, bring, aset, lds, ag, lslot, aload, t, s0, nst, nk16);
+    if (s0 + 1 < nst) kstage<NM, 1>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 1, nst, nk16);
+    if (s0 + 2 < nst) kstage<NM, 2>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 2, nst, nk16);
+    if (s0 + 3 < nst) kstage<NM, 3>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 3, nst, nk16);
+  }
+
+  // Epilogue through LDS: per 32-row fragment, each wavefront writes its 32 x 32
+  // (gate/up, after SwiGLU) or 32 x 64 (down) bf16 block row-major into its own 4 KiB of
+  // LDS, then stores whole 16-byte row pieces.
+  // 32x32 accumulator layout: element i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
+  // column l%32.
+  uint16_t* stage_out = reinterpret_cast<uint16_t*>(&lds[0][0]) + wave * 2048;
+  constexpr int ncol = GATE_UP ? 32 : 64;
+  constexpr int chunks = 32 * ncol / 8;  // 16-byte pieces per wavefront and fragment
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m * 32 >= t.rows) break;  // block-uniform
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int rr = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
+      if (GATE_UP) {
+        stage_out[rr * ncol + (lane & 31)] = to_bf16(silu_mul(acc[m][0][i], acc[m][1][i]));
+      } else {
+        stage_out[rr * ncol + (lane & 31)] = to_bf16(acc[m][0][i]);
+        stage_out[rr * ncol + 32 + (lane & 31)] = to_bf16(acc[m][1][i]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q0 = 0; q0 < chunks; q0 += 64) {
+      const int q = q0 + lane;
+      const int rr = q / (ncol / 8), cc = q % (ncol / 8);
+      const int r = m * 32 + rr;
+      if (t.act && r < t.rows)
+        *(uint4*)(t.out + (size_t)r * t.Nout + cc * 8) = *(const uint4*)(stage_out + rr * ncol + cc * 8);
+    }
+    __syncthreads();
+  }
+}
 
 template <bool GATE_UP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E,
                     const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout) {
-  __shared__ uint4 lds_a[2][16 * 64];  // [buf][(m32 * 4 + k16) * 64 + lane]
+  __shared__ uint4 lds_a[2][16 * 64];  // [buf][(m32 * 2 + k16) * 64 + lane]
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_wsum[4];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
 
-  // ---- per-expert M-tile starts (exclusive scan of ceil(count / 128))
+  // ---- per-expert M-tile starts (exclusive scan of ceil(count / 256))
   {
     const int per = div_up(E, 256);
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
@@ -90,14 +225,14 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
   const int total_mt = s_start[E];
   const int nk16 = K / 16;
   const int nf32 = Nout / 32;
-  const int ntn = GATE_UP ? div_up(nf32, 8) : div_up(nf32, 16);
+  const int ntn = GATE_UP ? div_up(nf32, 4) : div_up(nf32, 8);
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
   const int mt_lo = (int)((int64_t)total_mt * xcd / kXcds);
   const int mt_hi = (int)((int64_t)total_mt * (xcd + 1) / kXcds);
   const int items = (mt_hi - mt_lo) * ntn;
-  const int nst = K / 64;
+  const size_t panel = (size_t)nk16 * kOperandElems;
 
   for (int item = slot; item < items; item += nslots) {
     const int mt = mt_lo + item / ntn;
@@ -110,132 +245,35 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     }
     const int e = lo;
     const int row0 = offsets[e] + (mt - s_start[e]) * kPrefillBM;
-    const int rows = min(kPrefillBM, offsets[e + 1] - row0);
-
-    // this wavefront's 4 operand columns
-    const uint16_t* bs[4];
-    int fcol[4];
-    bool act[4];
-    const size_t panel = (size_t)nk16 * kOperandElems;
+    TileArgs t;
+    t.rows = min(kPrefillBM, offsets[e + 1] - row0);
+    t.K = K;
+    t.Nout = Nout;
+    t.wave = wave;
+    t.lane = lane;
+    int col0;
     if (GATE_UP) {
-      int af0 = (nt * 4 + wave) * 2;  // two 32-column groups of `a`
-      act[0] = act[1] = act[2] = act[3] = af0 < nf32;
-      af0 = min(af0, nf32 - 2);
-      const uint16_t* g0 = Bp + (size_t)(e * nf32 + af0) * 2 * panel;
-      bs[0] = g0;              // gate, columns af0
-      bs[1] = g0 + 2 * panel;  // gate, columns af0 + 1
-      bs[2] = g0 + panel;      // up,   columns af0
-      bs[3] = g0 + 3 * panel;  // up,   columns af0 + 1
-      fcol[0] = fcol[2] = af0 * 32;
-      fcol[1] = fcol[3] = af0 * 32 + 32;
+      int af = nt * 4 + wave;
+      t.act = af < nf32;
+      af = min(af, nf32 - 1);
+      t.b0 = Bp + (size_t)(e * nf32 + af) * 2 * panel;  // gate; up follows one panel later
+      col0 = af * 32;
     } else {
-      const int nf0 = (nt * 4 + wave) * 4;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        act[c] = nf0 + c < nf32;
-        const int f = min(nf0 + c, nf32 - 1);
-        bs[c] = Bp + (size_t)(e * nf32 + f) * panel;
-        fcol[c] = f * 32;
-      }
+      int nf = (nt * 4 + wave) * 2;
+      t.act = nf < nf32;
+      nf = min(nf, nf32 - 2);
+      t.b0 = Bp + (size_t)(e * nf32 + nf) * panel;  // second column one panel later
+      col0 = nf * 32;
     }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) bs[c] += lane * 8;
-
-    // activation stage loader: wavefront w fills the 4 operand fragments of rows
-    // 32w .. 32w+31 (one per k-step); lane L of the p-th load takes row 32w + L%32,
-    // k-offset 16p + 8*(L/32), so every LDS write is one contiguous 1 KiB fragment.
-    const uint16_t* ag[4];
-    int lslot[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = wave * 32 + (lane & 31);
-      ag[p] = A + (size_t)(row0 + min(r, rows - 1)) * K + p * 16 + (lane >> 5) * 8;
-      lslot[p] = (wave * 4 + p) * 64 + lane;
-    }
-
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[m][c] = f32x16_t{};
-
-    // b[kk][c]: operand column c of k-step kk of the current stage.  Each k-step's
-    // registers are refilled with the next stage's operands as soon as its MFMAs are
-    // issued, so a load has a whole stage (16 MFMAs x 4 k-steps) to land.
-    uint4 areg[4], b[4][4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) areg[p] = *(const uint4*)(ag[p]);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) b[kk][c] = *(const uint4*)(bs[c] + (size_t)kk * kOperandElems);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) lds_a[0][lslot[p]] = areg[p];
-    __syncthreads();
-
-    for (int st = 0; st < nst; ++st) {
-      const int cur = st & 1;
-      // Next stage's operands.  The loads are unconditional (the last stage reloads
-      // itself, into registers and a buffer nobody reads) so that the compiler cannot
-      // merge the load and the LDS store behind one branch and wait on the load at once.
-      const int sn = min(st + 1, nst - 1);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) areg[p] = *(const uint4*)(ag[p] + (size_t)sn * 64);
-      __builtin_amdgcn_sched_barrier(0);
-      bf16x8_t a[4], an[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(lds_a[cur][(m * 4 + 0) * 64 + lane]);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        // the next k-step's activation fragments are read before this k-step's MFMAs
-        if (kk < 3) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) an[m] = as_bf16x8(lds_a[cur][(m * 4 + kk + 1) * 64 + lane]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8_t bv = as_bf16x8(b[kk][c]);
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-            acc[m][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv, acc[m][c], 0, 0, 0);
-        }
-        const size_t o = (size_t)(sn * 4 + kk) * kOperandElems;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) b[kk][c] = *(const uint4*)(bs[c] + o);
-        if (kk < 3) {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) a[m] = an[m];
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p) lds_a[cur ^ 1][lslot[p]] = areg[p];
-      __syncthreads();
-    }
-
-    // 32x32 accumulator layout: element i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
-    // column l%32.
-    const int lc = lane & 31;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = m * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-        if (r >= rows) continue;
-        uint16_t* o = out + (size_t)(row0 + r) * Nout + lc;
-        if (GATE_UP) {
-          if (act[0]) {
-            o[fcol[0]] = to_bf16(silu_mul(acc[m][0][i], acc[m][2][i]));
-            o[fcol[1]] = to_bf16(silu_mul(acc[m][1][i], acc[m][3][i]));
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (act[c]) o[fcol[c]] = to_bf16(acc[m][c][i]);
-        }
-      }
-    }
+    t.b0 += lane * 8;
+    t.b1 = t.b0 + panel;
+    t.A = A + (size_t)row0 * K;
+    t.out = out + (size_t)row0 * Nout + col0;
+    const int nm = div_up(t.rows, 32);
+    if (nm > 6) prefill_tile<GATE_UP, 8>(t, lds_a);
+    else if (nm > 4) prefill_tile<GATE_UP, 6>(t, lds_a);
+    else if (nm > 2) prefill_tile<GATE_UP, 4>(t, lds_a);
+    else prefill_tile<GATE_UP, 2>(t, lds_a);
   }
 }
 
