@@ -28,7 +28,12 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(const uint4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
@@ -61,152 +66,207 @@ constexpr int kOperandElems = 512;  // one packed 32x16 (or 16x32) operand block
 // ------------------------------------------------------------------------------------
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
-constexpr int kRing = 8;  // weight ring depth in k-steps
+constexpr int kWaves = 8;               // wavefronts per block (two per SIMD)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRing = 4;                // weight ring depth in k-steps (one stage)
 
 struct TileArgs {
-  const uint16_t* A;     // activation rows of the tile (row0), row stride K
-  const uint16_t* b0;    // first operand column of this wavefront (lane offset applied)
+  const uint16_t* A;     // activation row row0 of the tile, row stride K
+  const uint16_t* b0;    // this wavefront's first operand column (lane offset applied)
   const uint16_t* b1;    // second operand column
   uint16_t* out;         // output row row0, column col0 (row stride Nout)
   int K, Nout, rows, wave, lane, act;
+  int fbase[4];          // LDS index of this lane's fragment piece, per k-step, m32 = 0
 };
 
-// One step of the k loop: MFMAs of k-step (2 * stage + KK) from LDS buffer BUF and ring
-// slot SLOT, then the ring slot is refilled with the operands KRING k-steps ahead.
-template <int NM, int BUF, int KK, int SLOT>
-__device__ __forceinline__ void kstep(f32x16_t (&acc)[8][2], uint4 (&bring)[kRing][2],
-                                      const uint4 (*lds)[16 * 64], const TileArgs& t,
-                                      int j_next) {
-  bf16x8_t a[NM];
+// LDS activation stage: 128 rows x 64 k bf16, row-major, 16-byte chunk c of row r stored
+// at chunk position c ^ (r & 7).  A wavefront store of 8 rows x 8 chunks and a fragment
+// read of 32 rows x 1 chunk both touch every bank once per 8 lanes.  Since fragment rows
+// start at multiples of 32, a lane's fragment piece for 32-row group m sits at
+// fbase[k-step] + 256 * m (uint4 units), and stage buffer b adds 1024 * b.
+__device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// k-step KK of a stage: MFMAs with activation fragments `a` and ring slot KK, then the
+// slot is refilled with operand k-step j_next; the next k-step's fragments are read
+// from LDS first so that their latency hides behind these MFMAs.
+template <int BUF, int KK>
+__device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
+                                      bf16x8_t (&a)[4], const u32x4 (*lds)[1024],
+                                      const TileArgs& t, int j_next) {
+  bf16x8_t an[4];
+  if (KK < 3) {
+    const u32x4* base = &lds[BUF][0] + t.fbase[KK + 1];
 #pragma unroll
-  for (int m = 0; m < NM; ++m) a[m] = as_bf16x8(lds[BUF][(m * 2 + KK) * 64 + t.lane]);
-  const bf16x8_t bv0 = as_bf16x8(bring[SLOT][0]);
-  const bf16x8_t bv1 = as_bf16x8(bring[SLOT][1]);
+    for (int m = 0; m < 4; ++m) an[m] = as_bf16x8(base[256 * m]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const bf16x8_t bv0 = as_bf16x8(bring[KK][0]);
+  const bf16x8_t bv1 = as_bf16x8(bring[KK][1]);
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
+  for (int m = 0; m < 4; ++m) {
     acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv0, acc[m][0], 0, 0, 0);
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv1, acc[m][1], 0, 0, 0);
   }
   const size_t o = (size_t)j_next * kOperandElems;
-  bring[SLOT][0] = *(const uint4*)(t.b0 + o);
-  bring[SLOT][1] = *(const uint4*)(t.b1 + o);
+  bring[KK][0] = *(const u32x4*)(t.b0 + o);
+  bring[KK][1] = *(const u32x4*)(t.b1 + o);
+  if (KK < 3) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) a[m] = an[m];
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One stage (two k-steps) with stage index s; U = s mod 4 picks registers and buffers.
-template <int NM, int U>
-__device__ __forceinline__ void kstage(f32x16_t (&acc)[8][2], uint4 (&bring)[kRing][2],
-                                       uint4 (&aset)[4][4], uint4 (*lds)[16 * 64],
-                                       const uint16_t* const (&ag)[4], const int (&lslot)[4],
-                                       bool (&aload)[4], const TileArgs& t, int s, int nst,
-                                       int nk16) {
-  const int sa = min(s + 3, nst - 1);
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    if (aload[p]) aset[(U + 3) & 3][p] = *(const uint4*)(ag[p] + (size_t)sa * 32);
+// One stage (4 k-steps of 16) from LDS buffer BUF.  Activations are loaded two stages
+// ahead into register set BUF and stored to LDS one stage ahead.
+template <int BUF>
+__device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
+                                       u32x4 (&aset0)[2], u32x4 (&aset1)[2],
+                                       u32x4 (*lds)[1024], const uint16_t* const (&ag)[2],
+                                       const int (&lslot)[2], const TileArgs& t, int s,
+                                       int nst) {
+  const size_t sa = (size_t)min(s + 2, nst - 1) * 64;
+  if constexpr (BUF == 0) {
+    aset0[0] = *(const u32x4*)(ag[0] + sa);
+    aset0[1] = *(const u32x4*)(ag[1] + sa);
+  } else {
+    aset1[0] = *(const u32x4*)(ag[0] + sa);
+    aset1[1] = *(const u32x4*)(ag[1] + sa);
+  }
   __builtin_amdgcn_sched_barrier(0);
-  kstep<NM, U & 1, 0, (2 * U) & 7>(acc, bring, lds, t, min(2 * s + kRing, nk16 - 1));
-  kstep<NM, U & 1, 1, (2 * U + 1) & 7>(acc, bring, lds, t, min(2 * s + 1 + kRing, nk16 - 1));
+  bf16x8_t a[4];
+  {
+    const u32x4* base = &lds[BUF][0] + t.fbase[0];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) lds[(U + 1) & 1][lslot[p]] = aset[(U + 1) & 3][p];
+    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(base[256 * m]);
+  }
+  // ring slots are refilled with the next stage's operands
+  const int jn = 4 * (s + 1), jmax = 4 * nst - 1;
+  kstep<BUF, 0>(acc, bring, a, lds, t, min(jn + 0, jmax));
+  kstep<BUF, 1>(acc, bring, a, lds, t, min(jn + 1, jmax));
+  kstep<BUF, 2>(acc, bring, a, lds, t, min(jn + 2, jmax));
+  kstep<BUF, 3>(acc, bring, a, lds, t, min(jn + 3, jmax));
+  // stage s + 1 (loaded at the start of stage s - 1) into the other buffer
+  if constexpr (BUF == 0) {
+    lds[1][lslot[0]] = aset1[0];
+    lds[1][lslot[1]] = aset1[1];
+  } else {
+    lds[0][lslot[0]] = aset0[0];
+    lds[0][lslot[1]] = aset0[1];
+  }
   __syncthreads();
 }
 
-// A whole work item with NM live 32-row fragments (NM = 2, 4, 6 or 8).
-template <bool GATE_UP, int NM>
-__device__ __forceinline__ void prefill_tile(const TileArgs& t, uint4 (*lds)[16 * 64]) {
-  const int nk16 = t.K / 16, nst = t.K / 32;
+// One work item: 128 rows x (this wavefront's two operand columns).
+template <bool GATE_UP>
+__device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[1024]) {
+  const int nst = t.K / 64;
   const int lane = t.lane, wave = t.wave;
-  // activation loader: wavefront w fills fragments (m32 = 2w + p/2, k16 = p%2); lane L
-  // takes row 32*m32 + L%32, k-offset 16*(p%2) + 8*(L/32): one contiguous LDS store each
-  const uint16_t* ag[4];
-  int lslot[4];
-  bool aload[4];
+  // activation loader: the p-th load of wavefront w covers rows 64p + 8w .. + 7, lane L
+  // taking chunk L % 8 of row L / 8: whole 128-byte lines
+  const uint16_t* ag[2];
+  int lslot[2];
+  const int lr = wave * 8 + (lane >> 3), lc = lane & 7;
+  const int lbase = a_slot(lr, lc);  // rows 64p + lr share (r & 7): slot lbase + 512p
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int mf = 2 * wave + (p >> 1), kf = p & 1;
-    const int r = mf * 32 + (lane & 31);
-    ag[p] = t.A + (size_t)min(r, t.rows - 1) * t.K + kf * 16 + (lane >> 5) * 8;
-    lslot[p] = (mf * 2 + kf) * 64 + lane;
-    aload[p] = mf < NM;
+  for (int p = 0; p < 2; ++p) {
+    ag[p] = t.A + (size_t)min(p * 64 + lr, t.rows - 1) * t.K + lc * 8;
+    lslot[p] = lbase + 512 * p;
   }
-  f32x16_t acc[8][2];
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int m = 0; m < 8; ++m) acc[m][0] = acc[m][1] = f32x16_t{};
-  uint4 aset[4][4];
-  uint4 bring[kRing][2];
-#pragma unroll
-  for (int u = 0; u < 3; ++u) {
-    const int st = min(u, nst - 1);
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      aset[u][p] = aload[p] ? *(const uint4*)(ag[p] + (size_t)st * 32) : uint4{0, 0, 0, 0};
-  }
-  aset[3][0] = aset[3][1] = aset[3][2] = aset[3][3] = uint4{0, 0, 0, 0};
+  for (int m = 0; m < 4; ++m) acc[m][0] = acc[m][1] = f32x16_t{};
+  u32x4 aset0[2], aset1[2];
+  u32x4 bring[kRing][2];
+  const size_t s1 = (size_t)min(1, nst - 1) * 64;
+  aset0[0] = *(const u32x4*)(ag[0]);
+  aset0[1] = *(const u32x4*)(ag[1]);
+  aset1[0] = *(const u32x4*)(ag[0] + s1);
+  aset1[1] = *(const u32x4*)(ag[1] + s1);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) {
-    const size_t o = (size_t)min(q, nk16 - 1) * kOperandElems;
-    bring[q][0] = *(const uint4*)(t.b0 + o);
-    bring[q][1] = *(const uint4*)(t.b1 + o);
+    const size_t o = (size_t)min(q, 4 * nst - 1) * kOperandElems;
+    bring[q][0] = *(const u32x4*)(t.b0 + o);
+    bring[q][1] = *(const u32x4*)(t.b1 + o);
   }
-#pragma unroll
-  for (int p = 0; p < 4; ++p) lds[0][lslot[p]] = aset[0][p];
+  lds[0][lslot[0]] = aset0[0];
+  lds[0][lslot[1]] = aset0[1];
   __syncthreads();
-  for (int s0 = 0; s0 < nst; s0 += 4) {
-    kstage<NM, 0>(acc, bring, aset, lds, ag, lslot, aload, t, s0, nst, nk16);
-    if (s0 + 1 < nst) kstage<NM, 1>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 1, nst, nk16);
-    if (s0 + 2 < nst) kstage<NM, 2>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 2, nst, nk16);
-    if (s0 + 3 < nst) kstage<NM, 3>(acc, bring, aset, lds, ag, lslot, aload, t, s0 + 3, nst, nk16);
+  for (int s0 = 0; s0 < nst; s0 += 2) {
+    kstage<0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+    if (s0 + 1 < nst) kstage<1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
   }
 
-  // Epilogue through LDS: per 32-row fragment, each wavefront writes its 32 x 32
-  // (gate/up, after SwiGLU) or 32 x 64 (down) bf16 block row-major into its own 4 KiB of
-  // LDS, then stores whole 16-byte row pieces.
+  // Epilogue through LDS: per 32-row fragment, each wavefront writes its 32 x 32 (gate/up,
+  // after SwiGLU) or 32 x 64 (down) bf16 block row-major into its own 4 KiB of LDS, then
+  // stores whole 16-byte row pieces.
   // 32x32 accumulator layout: element i of lane l is row 8*(i/4) + 4*(l/32) + i%4,
   // column l%32.
-  uint16_t* stage_out = reinterpret_cast<uint16_t*>(&lds[0][0]) + wave * 2048;
   constexpr int ncol = GATE_UP ? 32 : 64;
   constexpr int chunks = 32 * ncol / 8;  // 16-byte pieces per wavefront and fragment
+  uint16_t* const lds16 = reinterpret_cast<uint16_t*>(&lds[0][0]) + wave * 2048;
+  const int wofs = (lane >> 5) * 4 * ncol + (lane & 31);  // element (row 4*(l/32), col l%32)
+  const int qrow = lane / (ncol / 8), qcol = (lane % (ncol / 8)) * 8;
 #pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    if (m * 32 >= t.rows) break;  // block-uniform
+  for (int m = 0; m < 4; ++m) {
+    if (m * 32 < t.rows) {  // block-uniform
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rr = (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-      if (GATE_UP) {
-        stage_out[rr * ncol + (lane & 31)] = to_bf16(silu_mul(acc[m][0][i], acc[m][1][i]));
-      } else {
-        stage_out[rr * ncol + (lane & 31)] = to_bf16(acc[m][0][i]);
-        stage_out[rr * ncol + 32 + (lane & 31)] = to_bf16(acc[m][1][i]);
+      for (int i = 0; i < 16; ++i) {
+        uint16_t* srow = lds16 + wofs + ((i >> 2) * 8 + (i & 3)) * ncol;
+        if (GATE_UP) {
+          srow[0] = to_bf16(silu_mul(acc[m][0][i], acc[m][1][i]));
+        } else {
+          srow[0] = to_bf16(acc[m][0][i]);
+          srow[32] = to_bf16(acc[m][1][i]);
+        }
       }
-    }
-    __syncthreads();
+      __syncthreads();
 #pragma unroll
-    for (int q0 = 0; q0 < chunks; q0 += 64) {
-      const int q = q0 + lane;
-      const int rr = q / (ncol / 8), cc = q % (ncol / 8);
-      const int r = m * 32 + rr;
-      if (t.act && r < t.rows)
-        *(uint4*)(t.out + (size_t)r * t.Nout + cc * 8) = *(const uint4*)(stage_out + rr * ncol + cc * 8);
+      for (int q0 = 0; q0 < chunks; q0 += 64) {
+        const int rr = qrow + q0 / (ncol / 8);
+        const int r = m * 32 + rr;
+        if (t.act && r < t.rows)
+          *(u32x4*)(t.out + (size_t)r * t.Nout + qcol) = *(const u32x4*)(lds16 + rr * ncol + qcol);
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
+// ------------------------------------------------------------------------------------
+// Prefill grouped GEMM: persistent, one block of 8 wavefronts per CU.
+//
+// Work item = (M tile of 128 rows of one expert, N group).  Wavefront w computes the
+// tile's 128 rows for 2 operand columns (64 GEMM columns):
+//   GATE_UP: the gate and the up column of 32 outputs of `a` -> block: 256 columns of a
+//   DOWN   : 64 columns of yp                               -> block: 512 columns of yp
+// 4 x 2 accumulators of 32x32 (128 fp32 per lane, in AGPRs).
+//
+// K runs in stages of 64 (4 MFMA k-steps of 16).  The 128x64 activation stage goes
+// through LDS (double buffer, XOR-swizzled rows, loaded as whole 128-byte lines two
+// stages ahead); each wavefront's weight operands come straight from memory into a
+// one-stage register ring (each k-step's slot refilled as soon as its MFMAs issue).
+//
+// Scheduling: every block first turns `offsets` into per-expert M-tile starts (LDS).  The
+// M tiles are split into 8 contiguous ranges, one per XCD (workgroups are dispatched to
+// XCDs round-robin, so block b runs on XCD b % 8); the blocks of an XCD take its work
+// items in turn.  Items of one expert therefore run together on one XCD, and the weight
+// and activation bytes they share are served by that XCD's L2.
+// ------------------------------------------------------------------------------------
 template <bool GATE_UP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E,
                     const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout) {
-  __shared__ uint4 lds_a[2][16 * 64];  // [buf][(m32 * 2 + k16) * 64 + lane]
+  __shared__ u32x4 lds_a[2][1024];  // two activation stages (see a_slot)
   __shared__ int s_start[kMaxExperts + 1];
-  __shared__ int s_wsum[4];
+  __shared__ int s_wsum[kWaves];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
 
-  // ---- per-expert M-tile starts (exclusive scan of ceil(count / 256))
+  // ---- per-expert M-tile starts (exclusive scan of ceil(count / 128))
   {
-    const int per = div_up(E, 256);
+    const int per = div_up(E, kThreads);
     const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
     int sum = 0;
     for (int e = e0; e < e1; ++e) sum += div_up(offsets[e + 1] - offsets[e], kPrefillBM);
@@ -219,13 +279,13 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
       s_start[e] = base;
       base += div_up(offsets[e + 1] - offsets[e], kPrefillBM);
     }
-    if (tid == 255) s_start[E] = base;
+    if (tid == kThreads - 1) s_start[E] = base;
     __syncthreads();
   }
   const int total_mt = s_start[E];
   const int nk16 = K / 16;
   const int nf32 = Nout / 32;
-  const int ntn = GATE_UP ? div_up(nf32, 4) : div_up(nf32, 8);
+  const int ntn = GATE_UP ? div_up(nf32, kWaves) : div_up(nf32, 2 * kWaves);
   const int xcd = blockIdx.x % kXcds;
   const int slot = blockIdx.x / kXcds;
   const int nslots = gridDim.x / kXcds;
@@ -250,30 +310,35 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     t.K = K;
     t.Nout = Nout;
     t.wave = wave;
-    t.lane = lane;
+    // lane goes through an empty asm statement so that nothing derived from it is
+    // invariant across work items (the compiler would otherwise hoist the per-lane
+    // addresses of the epilogue out of this loop and keep them live through the k loop)
+    int lane_v = lane;
+    __asm__ volatile("" : "+v"(lane_v));
+    t.lane = lane_v;
     int col0;
     if (GATE_UP) {
-      int af = nt * 4 + wave;
+      int af = nt * kWaves + wave;  // 32 columns of `a`: gate and up operand columns
       t.act = af < nf32;
       af = min(af, nf32 - 1);
-      t.b0 = Bp + (size_t)(e * nf32 + af) * 2 * panel;  // gate; up follows one panel later
+      t.b0 = Bp + (size_t)(e * nf32 + af) * 2 * panel;
+      t.b1 = t.b0 + panel;
       col0 = af * 32;
     } else {
-      int nf = (nt * 4 + wave) * 2;
+      int nf = (nt * kWaves + wave) * 2;  // 64 columns of yp
       t.act = nf < nf32;
       nf = min(nf, nf32 - 2);
-      t.b0 = Bp + (size_t)(e * nf32 + nf) * panel;  // second column one panel later
+      t.b0 = Bp + (size_t)(e * nf32 + nf) * panel;
+      t.b1 = t.b0 + panel;
       col0 = nf * 32;
     }
-    t.b0 += lane * 8;
-    t.b1 = t.b0 + panel;
+    t.b0 += lane_v * 8;
+    t.b1 += lane_v * 8;
     t.A = A + (size_t)row0 * K;
     t.out = out + (size_t)row0 * Nout + col0;
-    const int nm = div_up(t.rows, 32);
-    if (nm > 6) prefill_tile<GATE_UP, 8>(t, lds_a);
-    else if (nm > 4) prefill_tile<GATE_UP, 6>(t, lds_a);
-    else if (nm > 2) prefill_tile<GATE_UP, 4>(t, lds_a);
-    else prefill_tile<GATE_UP, 2>(t, lds_a);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
+    prefill_tile<GATE_UP>(t, lds_a);
   }
 }
 
@@ -379,7 +444,7 @@ hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32
                        (const uint16_t*)xp, offsets, (const uint16_t*)packed_gu, (uint16_t*)a,
                        p.H, p.I);
   } else {
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(persistent_grid()), dim3(256), 0, s,
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3(persistent_grid()), dim3(kThreads), 0, s,
                        (const uint16_t*)xp, offsets, p.E, (const uint16_t*)packed_gu,
                        (uint16_t*)a, p.H, p.I);
   }
@@ -394,7 +459,7 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
                        (const uint16_t*)a, offsets, (const uint16_t*)packed_d, (uint16_t*)yp,
                        p.I, p.H);
   } else {
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(persistent_grid()), dim3(256), 0, s,
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3(persistent_grid()), dim3(kThreads), 0, s,
                        (const uint16_t*)a, offsets, p.E, (const uint16_t*)packed_d,
                        (uint16_t*)yp, p.I, p.H);
   }

@@ -12,7 +12,7 @@ namespace moe {
 // Tokens per routing chunk: one wavefront, one bit per token in a 64-bit mask.
 constexpr int kChunk = 64;
 // Rows per M tile of the prefill grouped GEMM.
-constexpr int kPrefillBM = 256;
+constexpr int kPrefillBM = 128;
 
 __host__ __device__ inline int div_up(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
