@@ -80,11 +80,15 @@ struct TileArgs {
 };
 
 // LDS activation stage: 128 rows x 64 k bf16, row-major, 16-byte chunk c of row r stored
-// at chunk position c ^ (r & 7).  A wavefront store of 8 rows x 8 chunks and a fragment
-// read of 32 rows x 1 chunk both touch every bank once per 8 lanes.  Since fragment rows
-// start at multiples of 32, a lane's fragment piece for 32-row group m sits at
+// at chunk position c ^ f(r), f(r) = ((r >> 1) ^ (r << 2)) & 7.  f takes 8 distinct values
+// on any 8 consecutive rows and on the even (and the odd) rows of any 16, so a wavefront
+// store of 8 rows x 8 chunks and a fragment read of 32 rows x 1 chunk are free of bank
+// conflicts whether the LDS serves 8 or 16 lanes of 16-byte accesses per cycle.  f depends
+// on r mod 16 only: a lane's fragment piece for 32-row group m sits at
 // fbase[k-step] + 256 * m (uint4 units), and stage buffer b adds 1024 * b.
-__device__ __forceinline__ int a_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+__device__ __forceinline__ int a_slot(int r, int c) {
+  return r * 8 + (c ^ (((r >> 1) ^ (r << 2)) & 7));
+}
 
 // k-step KK of a stage: MFMAs with activation fragments `a` and ring slot KK, then the
 // slot is refilled with operand k-step j_next; the next k-step's fragments are read
@@ -167,7 +171,7 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   const uint16_t* ag[2];
   int lslot[2];
   const int lr = wave * 8 + (lane >> 3), lc = lane & 7;
-  const int lbase = a_slot(lr, lc);  // rows 64p + lr share (r & 7): slot lbase + 512p
+  const int lbase = a_slot(lr, lc);  // rows 64p + lr share f(r): slot lbase + 512p
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
     ag[p] = t.A + (size_t)min(p * 64 + lr, t.rows - 1) * t.K + lc * 8;
