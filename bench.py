@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
+                         "for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -135,6 +138,15 @@ def main():
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 2, "launches": 3}), flush=True)
+        return
 
     import expert_ffn_moe_amd as moe
     import synth
