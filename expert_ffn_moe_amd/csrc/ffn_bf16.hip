@@ -93,7 +93,7 @@ __device__ __forceinline__ int a_slot(int r, int c) {
 // k-step KK of a stage: MFMAs with activation fragments `a` and ring slot KK, then the
 // slot is refilled with operand k-step j_next; the next k-step's fragments are read
 // from LDS first so that their latency hides behind these MFMAs.
-template <int BUF, int KK>
+template <int NM, int BUF, int KK>
 __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                       bf16x8_t (&a)[4], const u32x4 (*lds)[1024],
                                       const TileArgs& t, int j_next) {
@@ -101,13 +101,13 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
   if (KK < 3) {
     const u32x4* base = &lds[BUF][0] + t.fbase[KK + 1];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) an[m] = as_bf16x8(base[256 * m]);
+    for (int m = 0; m < NM; ++m) an[m] = as_bf16x8(base[256 * m]);
   }
   __builtin_amdgcn_sched_barrier(0);
   const bf16x8_t bv0 = as_bf16x8(bring[KK][0]);
   const bf16x8_t bv1 = as_bf16x8(bring[KK][1]);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < NM; ++m) {
     acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv0, acc[m][0], 0, 0, 0);
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv1, acc[m][1], 0, 0, 0);
   }
@@ -116,14 +116,14 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
   bring[KK][1] = *(const u32x4*)(t.b1 + o);
   if (KK < 3) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = an[m];
+    for (int m = 0; m < NM; ++m) a[m] = an[m];
   }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 // One stage (4 k-steps of 16) from LDS buffer BUF.  Activations are loaded two stages
 // ahead into register set BUF and stored to LDS one stage ahead.
-template <int BUF>
+template <int NM, int BUF>
 __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                        u32x4 (&aset0)[2], u32x4 (&aset1)[2],
                                        u32x4 (*lds)[1024], const uint16_t* const (&ag)[2],
@@ -142,14 +142,14 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
   {
     const u32x4* base = &lds[BUF][0] + t.fbase[0];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(base[256 * m]);
+    for (int m = 0; m < NM; ++m) a[m] = as_bf16x8(base[256 * m]);
   }
   // ring slots are refilled with the next stage's operands
   const int jn = 4 * (s + 1), jmax = 4 * nst - 1;
-  kstep<BUF, 0>(acc, bring, a, lds, t, min(jn + 0, jmax));
-  kstep<BUF, 1>(acc, bring, a, lds, t, min(jn + 1, jmax));
-  kstep<BUF, 2>(acc, bring, a, lds, t, min(jn + 2, jmax));
-  kstep<BUF, 3>(acc, bring, a, lds, t, min(jn + 3, jmax));
+  kstep<NM, BUF, 0>(acc, bring, a, lds, t, min(jn + 0, jmax));
+  kstep<NM, BUF, 1>(acc, bring, a, lds, t, min(jn + 1, jmax));
+  kstep<NM, BUF, 2>(acc, bring, a, lds, t, min(jn + 2, jmax));
+  kstep<NM, BUF, 3>(acc, bring, a, lds, t, min(jn + 3, jmax));
   // stage s + 1 (loaded at the start of stage s - 1) into the other buffer
   if constexpr (BUF == 0) {
     lds[1][lslot[0]] = aset1[0];
@@ -196,9 +196,16 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   lds[0][lslot[0]] = aset0[0];
   lds[0][lslot[1]] = aset0[1];
   __syncthreads();
-  for (int s0 = 0; s0 < nst; s0 += 2) {
-    kstage<0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
-    if (s0 + 1 < nst) kstage<1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+  if (t.rows > 64) {  // block-uniform: a tile with at most 64 live rows skips the others
+    for (int s0 = 0; s0 < nst; s0 += 2) {
+      kstage<4, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      if (s0 + 1 < nst) kstage<4, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+    }
+  } else {
+    for (int s0 = 0; s0 < nst; s0 += 2) {
+      kstage<2, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      if (s0 + 1 < nst) kstage<2, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+    }
   }
 
   // Epilogue through LDS: per 32-row fragment, each wavefront writes its 32 x 32 (gate/up,
