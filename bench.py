@@ -1,9 +1,13 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic tokens:
-  moe_route -> moe_dispatch -> moe_expert_gate_up -> moe_expert_down -> moe_combine
-(capacity selection runs inside moe_route when the workload has a cap).  Inputs and the
-packed expert weights are resident in HBM before timing starts.
+One step = one pass of the whole path over one batch of synthetic tokens, the kernel
+sequence of moe_layer issued through the staged entry points so that every stage can be
+timed:
+  moe_route -> moe_dispatch (layout only) -> moe_expert_gate_up_gather -> moe_expert_down
+  -> moe_combine
+(capacity selection runs inside moe_route when the workload has a cap; gate/up reads the
+token rows through row_token, so no permuted copy of x is written).  Inputs and the packed
+expert weights are resident in HBM before timing starts.
 
 Prints one JSON line: whole-step throughput in tokens/s, the roofline of the dominant
 kernel (per-launch algorithmic bytes or flops over its HIP-event-timed duration on the
@@ -42,13 +46,17 @@ def parse():
 
 
 def algorithmic(wl, N, E_hit):
-    """Per-launch algorithmic HBM bytes and flops of each stage (decimal units)."""
+    """Per-launch algorithmic HBM bytes and flops of each stage (decimal units): every input
+    read once and every output written once."""
     b = 2 if wl.dtype == "bf16" else 4
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     return {
         "route": dict(bytes=T * E * 4 + T * k * 9, flops=0),
-        "dispatch": dict(bytes=T * k * 5 + T * H * b + N * H * b + N * 8 + E * 8, flops=0),
-        "gate_up": dict(bytes=E_hit * 2 * H * I * b + N * H * b + N * I * b, flops=4 * N * H * I),
+        # ids (+ keep) in; counts, offsets, row_token, slot_to_row out
+        "dispatch": dict(bytes=T * k * 5 + N * 4 + T * k * 4 + E * 8, flops=0),
+        # weights of the experts hit, the token rows x (once) and row_token in; a out
+        "gate_up": dict(bytes=E_hit * 2 * H * I * b + T * H * b + N * 4 + N * I * b,
+                        flops=4 * N * H * I),
         "down": dict(bytes=E_hit * I * H * b + N * I * b + N * H * b, flops=2 * N * H * I),
         "combine": dict(bytes=N * H * b + T * k * 8 + T * H * b, flops=0),
     }
@@ -167,8 +175,7 @@ def main():
     disp = dict(counts=torch.empty(wl.E, dtype=torch.int32, device=dev),
                 offsets=torch.empty(wl.E + 1, dtype=torch.int32, device=dev),
                 row_token=torch.empty(tk, dtype=torch.int32, device=dev),
-                slot_to_row=torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev),
-                xp=torch.empty(tk, wl.H, dtype=dt, device=dev))
+                slot_to_row=torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev), xp=None)
     a = torch.empty(tk, wl.I, dtype=dt, device=dev)
     yp = torch.empty(tk, wl.H, dtype=dt, device=dev)
     y = torch.empty(wl.T, wl.H, dtype=dt, device=dev)
@@ -181,9 +188,10 @@ def main():
         mark(0)
         ids, w, keep = moe.route(p, inp["logits"], out=routing, ws=ws[moe.OP_ROUTE])
         mark(1)
-        moe.dispatch(p, inp["x"], ids, keep if wl.capacity > 0 else None, out=disp, ws=ws[moe.OP_DISPATCH])
+        moe.dispatch(p, inp["x"], ids, keep if wl.capacity > 0 else None, out=disp,
+                     ws=ws[moe.OP_DISPATCH], rows=False)
         mark(2)
-        moe.expert_gate_up(p, disp["xp"], disp["offsets"], pgu, out=a, ws=ws[moe.OP_FFN])
+        moe.expert_gate_up_gather(p, inp["x"], disp["row_token"], disp["offsets"], pgu, out=a)
         mark(3)
         moe.expert_down(p, a, disp["offsets"], pd, out=yp, ws=ws[moe.OP_FFN])
         mark(4)

@@ -6,8 +6,8 @@ calls the C ABI declared in include/moe.h on torch's current HIP stream.  All co
 in the library's HIP kernels; if libmoe.so is missing or fails to load, importing this
 package raises -- there is no other implementation.
 
-Call names follow the C ABI: route, dispatch, expert_gate_up, expert_down, expert_ffn,
-combine, layer, plus pack_weights for the one-time weight packing.
+Call names follow the C ABI: route, dispatch, expert_gate_up, expert_gate_up_gather,
+expert_down, expert_ffn, combine, layer, plus pack_weights for the one-time weight packing.
 """
 from __future__ import annotations
 
@@ -28,6 +28,7 @@ W_GATE_UP, W_DOWN = 0, 1
 
 EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_packed_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
+           "moe_expert_gate_up_gather",
            "moe_expert_down", "moe_combine", "moe_layer")
 
 
@@ -60,6 +61,7 @@ def _load() -> ctypes.CDLL:
         "moe_dispatch": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, sz, P]),
         "moe_expert_ffn": (ctypes.c_int, [PP, P, P, P, P, P, P, sz, P]),
         "moe_expert_gate_up": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
+        "moe_expert_gate_up_gather": (ctypes.c_int, [PP, P, P, P, P, P, P, sz, P]),
         "moe_expert_down": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
         "moe_combine": (ctypes.c_int, [PP, P, P, P, P, P]),
         "moe_layer": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
@@ -184,8 +186,8 @@ def route(p: Problem, logits, out=None, ws=None):
     return ids, w, keep
 
 
-def dispatch(p: Problem, x, topk_ids, keep=None, out=None, ws=None):
-    """Expert-contiguous layout + row gather.
+def dispatch(p: Problem, x, topk_ids, keep=None, out=None, ws=None, rows=True):
+    """Expert-contiguous layout + row gather (rows=False: the layout only, xp is None).
     Returns dict(counts, offsets, row_token, slot_to_row, xp)."""
     dt = p.torch_dtype
     _need(x, "x", (p.T, p.H), dt)
@@ -197,7 +199,10 @@ def dispatch(p: Problem, x, topk_ids, keep=None, out=None, ws=None):
     if out is None:
         out = dict(counts=_empty((p.E,), torch.int32, dev), offsets=_empty((p.E + 1,), torch.int32, dev),
                    row_token=_empty((tk,), torch.int32, dev),
-                   slot_to_row=_empty((p.T, p.k), torch.int32, dev), xp=_empty((tk, p.H), dt, dev))
+                   slot_to_row=_empty((p.T, p.k), torch.int32, dev),
+                   xp=_empty((tk, p.H), dt, dev) if rows else None)
+    elif not rows:
+        out = dict(out, xp=None)
     ws = workspace(p, OP_DISPATCH, dev) if ws is None else ws
     c = p.c()
     _call("moe_dispatch", ctypes.byref(c), _ptr(x), _ptr(topk_ids), _ptr(keep), _ptr(out["counts"]),
@@ -217,6 +222,20 @@ def expert_gate_up(p: Problem, xp, offsets, packed_gate_up, out=None, ws=None):
     c = p.c()
     _call("moe_expert_gate_up", ctypes.byref(c), _ptr(xp), _ptr(offsets), _ptr(packed_gate_up),
           _ptr(a), _ptr(ws), ws.numel(), _stream())
+    return a
+
+
+def expert_gate_up_gather(p: Problem, x, row_token, offsets, packed_gate_up, out=None, ws=None):
+    """expert_gate_up with the rows read as x[row_token[r]] (no xp); returns a [T*k, I]."""
+    dt = p.torch_dtype
+    tk = p.T * p.k
+    _need(x, "x", (p.T, p.H), dt)
+    _need(row_token, "row_token", (tk,), torch.int32)
+    _need(offsets, "offsets", (p.E + 1,), torch.int32)
+    a = _empty((tk, p.I), dt, x.device) if out is None else out
+    c = p.c()
+    _call("moe_expert_gate_up_gather", ctypes.byref(c), _ptr(x), _ptr(row_token), _ptr(offsets),
+          _ptr(packed_gate_up), _ptr(a), None, 0, _stream())
     return a
 
 

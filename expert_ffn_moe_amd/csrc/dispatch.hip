@@ -81,32 +81,49 @@ __global__ __launch_bounds__(1024) void scan_cols_kernel(const int32_t* __restri
   }
 }
 
-// offsets = exclusive scan of counts (E <= 1024, one block).
-__global__ __launch_bounds__(1024) void scan_experts_kernel(const int32_t* __restrict__ counts,
-                                                            int E,
-                                                            int32_t* __restrict__ offsets) {
-  __shared__ int wsum[16];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = threadIdx.x;
-  const int v = e < E ? counts[e] : 0;
-  const int inc = wave_inclusive_scan(v);
+// Exclusive scan of counts[0..E) into s_off[0..E] (E <= kMaxE = 1024), by a block of 256
+// threads (4 experts per thread).  Contains barriers: call from every thread of the block.
+__device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts, int E,
+                                              int* s_off) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int v[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    v[i] = e < E ? counts[e] : 0;
+    sum += v[i];
+  }
+  const int inc = wave_inclusive_scan(sum);
   if (lane == 63) wsum[wave] = inc;
   __syncthreads();
-  int base = 0;
+  int base = inc - sum;
   for (int w = 0; w < wave; ++w) base += wsum[w];
-  if (e < E) offsets[e] = base + inc - v;
-  if (e == E - 1) offsets[E] = base + inc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = tid * 4 + i;
+    if (e < E) s_off[e] = base;
+    base += v[i];
+  }
+  if (tid == 255) s_off[E] = base;  // the last thread ends with the total
+  __syncthreads();
 }
 
+// Every block scans the counts into offsets itself (E <= 1024 values, cheaper than a
+// launch of its own); block 0 also writes them out.
 template <bool HAS_KEEP, bool CAND>
 __global__ __launch_bounds__(256) void scatter_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ keep, int T, int E, int k,
-    int nchunks, const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ row_token, int32_t* __restrict__ slot_to_row,
-    int32_t* __restrict__ cand_slot) {
+    int nchunks, const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
+    int32_t* __restrict__ slot_to_row, int32_t* __restrict__ cand_slot) {
   extern __shared__ uint64_t smem_bm[];
+  __shared__ int s_off[kMaxE + 4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + wave;
+  block_offsets(counts, E, s_off);
+  if (blockIdx.x == 0)
+    for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
   uint64_t* bm = smem_bm + (size_t)wave * E;
   build_chunk_bitmap<HAS_KEEP>(bm, ids, keep, T, E, k, c, nchunks);
   const int t = c * kChunk + lane;
@@ -116,7 +133,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
     const size_t s = (size_t)t * k + j;
     const int e = ids[s];
     if (!HAS_KEEP || keep[s]) {
-      const int row = offsets[e] + chunk_base[(size_t)c * E + e] + __popcll(bm[e] & below);
+      const int row = s_off[e] + chunk_base[(size_t)c * E + e] + __popcll(bm[e] & below);
       if (CAND) {
         cand_slot[row] = (int32_t)s;
       } else {
@@ -227,16 +244,15 @@ hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uin
 }
 
 hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
-                       int32_t* counts, int32_t* offsets, hipStream_t s) {
+                       int32_t* counts, hipStream_t s) {
   const int nchunks = div_up(p.T, kChunk);
   hipLaunchKernelGGL(scan_cols_kernel, dim3(div_up(p.E, 64)), dim3(1024), 0, s, chunk_hist,
                      p.E, nchunks, chunk_base, counts);
-  hipLaunchKernelGGL(scan_experts_kernel, dim3(1), dim3(1024), 0, s, counts, p.E, offsets);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                          const int32_t* chunk_base, const int32_t* offsets,
+                          const int32_t* chunk_base, const int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
                           hipStream_t s) {
   const int nchunks = div_up(p.T, kChunk);
@@ -244,16 +260,16 @@ hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_
   const size_t lds = bitmap_lds(p);
   if (cand_slot) {
     hipLaunchKernelGGL((scatter_kernel<false, true>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
-                       cand_slot);
+                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
+                       slot_to_row, cand_slot);
   } else if (keep) {
     hipLaunchKernelGGL((scatter_kernel<true, false>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
-                       cand_slot);
+                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
+                       slot_to_row, cand_slot);
   } else {
     hipLaunchKernelGGL((scatter_kernel<false, false>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, offsets, row_token, slot_to_row,
-                       cand_slot);
+                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
+                       slot_to_row, cand_slot);
   }
   return hipGetLastError();
 }

@@ -71,7 +71,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRing = 4;                // weight ring depth in k-steps (one stage)
 
 struct TileArgs {
-  const uint16_t* A;     // activation row row0 of the tile, row stride K
+  const uint16_t* A;     // activation row row0 of the tile, row stride K (with a row
+                         // gather: the token rows x, row i of the tile being rtok[i])
+  const int32_t* rtok;   // row gather only: row_token + row0
   const uint16_t* b0;    // this wavefront's first operand column (lane offset applied)
   const uint16_t* b1;    // second operand column
   uint16_t* out;         // output row row0, column col0 (row stride Nout)
@@ -162,7 +164,7 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
 }
 
 // One work item: 128 rows x (this wavefront's two operand columns).
-template <bool GATE_UP>
+template <bool GATE_UP, bool GATHER>
 __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[1024]) {
   const int nst = t.K / 64;
   const int lane = t.lane, wave = t.wave;
@@ -174,7 +176,9 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   const int lbase = a_slot(lr, lc);  // rows 64p + lr share f(r): slot lbase + 512p
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    ag[p] = t.A + (size_t)min(p * 64 + lr, t.rows - 1) * t.K + lc * 8;
+    const int r = min(p * 64 + lr, t.rows - 1);
+    const size_t src_row = GATHER ? (size_t)t.rtok[r] : (size_t)r;
+    ag[p] = t.A + src_row * t.K + lc * 8;
     lslot[p] = lbase + 512 * p;
   }
   f32x16_t acc[4][2];
@@ -264,9 +268,12 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
 // items in turn.  Items of one expert therefore run together on one XCD, and the weight
 // and activation bytes they share are served by that XCD's L2.
 // ------------------------------------------------------------------------------------
-template <bool GATE_UP>
+// GATHER (gate/up only): the activation rows are token rows x[row_token[r]] instead of
+// xp[r], so the dispatch row copy is folded into this kernel's activation loads.
+template <bool GATE_UP, bool GATHER>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ offsets, int E,
+void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+                    const int32_t* __restrict__ offsets, int E,
                     const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout) {
   __shared__ u32x4 lds_a[2][1024];  // two activation stages (see a_slot)
   __shared__ int s_start[kMaxExperts + 1];
@@ -345,11 +352,12 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     }
     t.b0 += lane_v * 8;
     t.b1 += lane_v * 8;
-    t.A = A + (size_t)row0 * K;
+    t.A = GATHER ? A : A + (size_t)row0 * K;
+    t.rtok = GATHER ? row_token + row0 : nullptr;
     t.out = out + (size_t)row0 * Nout + col0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
-    prefill_tile<GATE_UP>(t, lds_a);
+    prefill_tile<GATE_UP, GATHER>(t, lds_a);
   }
 }
 
@@ -358,8 +366,9 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
 //   GATE_UP: 32 columns of `a` (gate + up operand columns); DOWN: 64 columns of yp.
 // Each k-step of 32 issues 4 B operand loads (16 columns each) and one A load.
 // ------------------------------------------------------------------------------------
-template <bool GATE_UP>
+template <bool GATE_UP, bool GATHER>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A,
+                                                     const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
                                                      const uint16_t* __restrict__ Bp,
                                                      uint16_t* __restrict__ out, int K,
@@ -390,7 +399,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = f32x4_t{};
     const int ar = row_beg + min(m0 + (lane & 15), cnt - 1);
-    const uint16_t* ap = A + (size_t)ar * K + 8 * (lane >> 4);
+    const size_t src_row = GATHER ? (size_t)row_token[ar] : (size_t)ar;
+    const uint16_t* ap = A + src_row * K + 8 * (lane >> 4);
 #pragma unroll 4
     for (int ks = 0; ks < nks; ++ks) {
       const uint4 av = *(const uint4*)(ap + ks * 32);
@@ -447,18 +457,30 @@ int cu_count() {
 int persistent_grid() { return std::max(kXcds, cu_count() / kXcds * kXcds); }
 }  // namespace
 
-hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32_t* offsets,
-                               const void* packed_gu, void* a, hipStream_t s) {
+namespace {
+template <bool GATHER>
+void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
+                  const int32_t* offsets, const void* packed_gu, void* a, hipStream_t s) {
   if (ffn_use_decode(p)) {
     const int nf32 = p.I / 32;
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(div_up(nf32, 4), p.E), dim3(256), 0, s,
-                       (const uint16_t*)xp, offsets, (const uint16_t*)packed_gu, (uint16_t*)a,
-                       p.H, p.I);
-  } else {
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3(persistent_grid()), dim3(kThreads), 0, s,
-                       (const uint16_t*)xp, offsets, p.E, (const uint16_t*)packed_gu,
+    hipLaunchKernelGGL((decode_kernel<true, GATHER>), dim3(div_up(nf32, 4), p.E), dim3(256), 0,
+                       s, (const uint16_t*)xs, row_token, offsets, (const uint16_t*)packed_gu,
                        (uint16_t*)a, p.H, p.I);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<true, GATHER>), dim3(persistent_grid()), dim3(kThreads),
+                       0, s, (const uint16_t*)xs, row_token, offsets, p.E,
+                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I);
   }
+}
+}  // namespace
+
+hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
+                               const int32_t* offsets, const void* packed_gu, void* a,
+                               hipStream_t s) {
+  if (row_token)
+    gate_up_bf16<true>(p, xs, row_token, offsets, packed_gu, a, s);
+  else
+    gate_up_bf16<false>(p, xs, nullptr, offsets, packed_gu, a, s);
   return hipGetLastError();
 }
 
@@ -466,13 +488,13 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
                             const void* packed_d, void* yp, hipStream_t s) {
   if (ffn_use_decode(p)) {
     const int nf32 = p.H / 32;
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(div_up(nf32 / 2, 4), p.E), dim3(256), 0, s,
-                       (const uint16_t*)a, offsets, (const uint16_t*)packed_d, (uint16_t*)yp,
-                       p.I, p.H);
-  } else {
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3(persistent_grid()), dim3(kThreads), 0, s,
-                       (const uint16_t*)a, offsets, p.E, (const uint16_t*)packed_d,
+    hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
+                       0, s, (const uint16_t*)a, nullptr, offsets, (const uint16_t*)packed_d,
                        (uint16_t*)yp, p.I, p.H);
+  } else {
+    hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()), dim3(kThreads),
+                       0, s, (const uint16_t*)a, nullptr, offsets, p.E,
+                       (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H);
   }
   return hipGetLastError();
 }

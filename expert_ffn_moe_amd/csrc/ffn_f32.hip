@@ -1,6 +1,7 @@
 // Grouped SwiGLU expert FFN in fp32 (vector ALU, fp32 fused multiply-add).  Used for the
 // small fp32 problems; weights in the natural layout [E, H, I] / [E, I, H].
 //   a[r]  = silu(xp[r] Wg[e]) * (xp[r] Wu[e]);  yp[r] = a[r] Wd[e]
+// (with a row gather, x[row_token[r]] stands in for xp[r])
 // One thread per output element; the row's expert is found by binary search over offsets.
 #include "moe_internal.h"
 
@@ -18,6 +19,7 @@ __device__ __forceinline__ int expert_of_row(const int32_t* __restrict__ offsets
 }
 
 __global__ __launch_bounds__(256) void gate_up_f32_kernel(const float* __restrict__ xp,
+                                                          const int32_t* __restrict__ row_token,
                                                           const int32_t* __restrict__ offsets,
                                                           const float* __restrict__ wg,
                                                           const float* __restrict__ wu,
@@ -27,7 +29,7 @@ __global__ __launch_bounds__(256) void gate_up_f32_kernel(const float* __restric
   const int i = blockIdx.y * 64 + (threadIdx.x & 63);
   if (r >= offsets[E] || i >= I) return;
   const int e = expert_of_row(offsets, E, r);
-  const float* x = xp + (size_t)r * H;
+  const float* x = xp + (size_t)(row_token ? row_token[r] : r) * H;
   const float* g = wg + (size_t)e * H * I + i;
   const float* u = wu + (size_t)e * H * I + i;
   float sg = 0.f, su = 0.f;
@@ -57,11 +59,12 @@ __global__ __launch_bounds__(256) void down_f32_kernel(const float* __restrict__
 
 }  // namespace
 
-hipError_t launch_gate_up_f32(const moe_problem& p, const float* xp, const int32_t* offsets,
-                              const float* wg, const float* wu, float* a, hipStream_t s) {
+hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32_t* row_token,
+                              const int32_t* offsets, const float* wg, const float* wu, float* a,
+                              hipStream_t s) {
   const int rows = p.T * p.k;
   hipLaunchKernelGGL(gate_up_f32_kernel, dim3(div_up(rows, 4), div_up(p.I, 64)), dim3(256), 0,
-                     s, xp, offsets, wg, wu, a, p.E, p.H, p.I);
+                     s, xs, row_token, offsets, wg, wu, a, p.E, p.H, p.I);
   return hipGetLastError();
 }
 

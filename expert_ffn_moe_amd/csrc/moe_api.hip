@@ -47,7 +47,7 @@ struct LayerScratch {
   int32_t *ids, *counts, *offsets, *row_token, *slot_to_row;
   float* w;
   uint8_t* keep;
-  void *xp, *yp;
+  void* yp;
   RankScratch rank;
   FfnScratch ffn;
 };
@@ -62,7 +62,6 @@ LayerScratch carve_layer(Carve& c, const moe_problem& p) {
   L.offsets = c.take<int32_t>((size_t)p.E + 1);
   L.row_token = c.take<int32_t>(tk);
   L.slot_to_row = c.take<int32_t>(tk);
-  L.xp = c.take<char>(tk * p.H * eb);
   L.yp = c.take<char>(tk * p.H * eb);
   L.rank = carve_rank(c, p, p.capacity > 0);
   L.ffn = carve_ffn(c, p);
@@ -108,11 +107,10 @@ hipError_t run_route(const moe_problem& p, const float* logits, int32_t* ids, fl
   hipError_t err = launch_route(p, logits, ids, w, keep, s);
   if (err != hipSuccess || p.capacity <= 0) return err;
   if ((err = launch_chunk_hist(p, ids, nullptr, r.chunk_hist, s)) != hipSuccess) return err;
-  if ((err = launch_scan(p, r.chunk_hist, r.chunk_base, r.cand_counts, r.cand_offsets, s)) !=
-      hipSuccess)
+  if ((err = launch_scan(p, r.chunk_hist, r.chunk_base, r.cand_counts, s)) != hipSuccess)
     return err;
-  if ((err = launch_scatter(p, ids, nullptr, r.chunk_base, r.cand_offsets, nullptr, nullptr,
-                            r.cand_slot, s)) != hipSuccess)
+  if ((err = launch_scatter(p, ids, nullptr, r.chunk_base, r.cand_counts, r.cand_offsets,
+                            nullptr, nullptr, r.cand_slot, s)) != hipSuccess)
     return err;
   return launch_capacity_select(p, r.cand_counts, r.cand_offsets, r.cand_slot, w, keep, s);
 }
@@ -122,22 +120,23 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
                         int32_t* row_token, int32_t* slot_to_row, void* xp,
                         const RankScratch& r, hipStream_t s) {
   hipError_t err = launch_chunk_hist(p, ids, keep, r.chunk_hist, s);
-  if (err == hipSuccess) err = launch_scan(p, r.chunk_hist, r.chunk_base, counts, offsets, s);
+  if (err == hipSuccess) err = launch_scan(p, r.chunk_hist, r.chunk_base, counts, s);
   if (err == hipSuccess)
-    err = launch_scatter(p, ids, keep, r.chunk_base, offsets, row_token, slot_to_row, nullptr,
-                         s);
-  if (err == hipSuccess) err = launch_gather(p, x, slot_to_row, xp, s);
+    err = launch_scatter(p, ids, keep, r.chunk_base, counts, offsets, row_token, slot_to_row,
+                         nullptr, s);
+  if (err == hipSuccess && xp) err = launch_gather(p, x, slot_to_row, xp, s);
   return err;
 }
 
-hipError_t run_gate_up(const moe_problem& p, const void* xp, const int32_t* offsets,
-                       const void* pgu, void* a, hipStream_t s) {
+// Gate/up over the layout: rows xs[r], or token rows xs[row_token[r]] if row_token != NULL.
+hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_token,
+                       const int32_t* offsets, const void* pgu, void* a, hipStream_t s) {
   if (p.act_dtype == MOE_F32) {
     const size_t n = (size_t)p.E * p.H * p.I;
-    return launch_gate_up_f32(p, (const float*)xp, offsets, (const float*)pgu,
+    return launch_gate_up_f32(p, (const float*)xs, row_token, offsets, (const float*)pgu,
                               (const float*)pgu + n, (float*)a, s);
   }
-  return launch_gate_up_bf16(p, xp, offsets, pgu, a, s);
+  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, s);
 }
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
@@ -170,7 +169,7 @@ int moe_problem_check(const moe_problem* p) {
       (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16))
     return MOE_ERR_INVALID_ARG;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
-  if (p->E > 1024 || p->k > 32) return MOE_ERR_UNSUPPORTED;
+  if (p->E > kMaxE || p->k > 32) return MOE_ERR_UNSUPPORTED;
   if (p->act_dtype != p->w_dtype) return MOE_ERR_UNSUPPORTED;
   const int mult = p->act_dtype == MOE_BF16 ? 64 : 8;
   if (p->H % mult || p->I % mult) return MOE_ERR_UNSUPPORTED;
@@ -220,9 +219,9 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
                  int32_t* slot_to_row, void* xp, void* ws, size_t ws_bytes, void* stream) {
   int st = moe_problem_check(p);
   if (st != MOE_OK) return st;
-  if (!x || !topk_ids || !counts || !offsets || !row_token || !slot_to_row || !xp)
+  if (!x || !topk_ids || !counts || !offsets || !row_token || !slot_to_row)
     return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(xp)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || (xp && !aligned16(xp))) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_DISPATCH, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   RankScratch r = carve_rank(c, *p, false);
@@ -239,7 +238,20 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
   if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
   (void)ws;
   (void)ws_bytes;
-  return status_of(run_gate_up(*p, xp, offsets, packed_gate_up, a, as_stream(stream)));
+  return status_of(run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, as_stream(stream)));
+}
+
+int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t* row_token,
+                              const int32_t* offsets, const void* packed_gate_up, void* a,
+                              void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!x || !row_token || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
+  (void)ws;
+  (void)ws_bytes;
+  return status_of(
+      run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, as_stream(stream)));
 }
 
 int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
@@ -267,7 +279,7 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   Carve c(ws);
   FfnScratch f = carve_ffn(c, *p);
   hipStream_t s = as_stream(stream);
-  hipError_t err = run_gate_up(*p, xp, offsets, packed_gate_up, f.a, s);
+  hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, s);
   if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, s);
   return status_of(err);
 }
@@ -303,10 +315,12 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if (!slot_to_row) slot_to_row = L.slot_to_row;
   hipStream_t s = as_stream(stream);
   hipError_t err = run_route(*p, logits, topk_ids, topk_w, keep, L.rank, s);
+  // dispatch builds the layout only: gate/up reads the token rows through row_token
   if (err == hipSuccess)
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
-                       row_token, slot_to_row, L.xp, L.rank, s);
-  if (err == hipSuccess) err = run_gate_up(*p, L.xp, offsets, packed_gate_up, L.ffn.a, s);
+                       row_token, slot_to_row, nullptr, L.rank, s);
+  if (err == hipSuccess)
+    err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, s);
   if (err == hipSuccess) err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, s);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, y, s);
   return status_of(err);

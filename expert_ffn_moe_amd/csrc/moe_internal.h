@@ -11,6 +11,8 @@ namespace moe {
 
 // Tokens per routing chunk: one wavefront, one bit per token in a 64-bit mask.
 constexpr int kChunk = 64;
+// Largest expert count the kernels handle (moe_problem_check).
+constexpr int kMaxE = 1024;
 // Rows per M tile of the prefill grouped GEMM.
 constexpr int kPrefillBM = 128;
 
@@ -48,13 +50,14 @@ hipError_t launch_route(const moe_problem& p, const float* logits, int32_t* ids,
 // Per-chunk histogram of (kept) assignments per expert.
 hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
                              int32_t* chunk_hist, hipStream_t s);
-// Column scan over chunks per expert -> chunk_base, counts; then offsets = scan(counts).
+// Column scan over chunks per expert -> chunk_base, counts.
 hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
-                       int32_t* counts, int32_t* offsets, hipStream_t s);
-// Stable scatter: row of each kept slot.  If cand_slot != NULL the rows index the slot
-// list cand_slot (capacity candidates) instead of writing row_token / slot_to_row.
+                       int32_t* counts, hipStream_t s);
+// Stable scatter: offsets = exclusive scan of counts (written out), then the row of each
+// kept slot.  If cand_slot != NULL the rows index the slot list cand_slot (capacity
+// candidates) instead of writing row_token / slot_to_row.
 hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                          const int32_t* chunk_base, const int32_t* offsets,
+                          const int32_t* chunk_base, const int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
                           hipStream_t s);
 // Capacity: per overflowing expert, radix-select the top-C keys and clear keep for the rest.
@@ -75,12 +78,16 @@ hipError_t launch_pack(const moe_problem& p, const void* wg, const void* wu, con
 
 // ---- ffn_bf16.hip / ffn_f32.hip
 bool ffn_use_decode(const moe_problem& p);
-hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xp, const int32_t* offsets,
-                               const void* packed_gu, void* a, hipStream_t s);
+// Gate/up over the layout's rows: row r reads xs[r] (xp), or xs[row_token[r]] (token rows
+// x) when row_token is not NULL.
+hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
+                               const int32_t* offsets, const void* packed_gu, void* a,
+                               hipStream_t s);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
                             const void* packed_d, void* yp, hipStream_t s);
-hipError_t launch_gate_up_f32(const moe_problem& p, const float* xp, const int32_t* offsets,
-                              const float* wg, const float* wu, float* a, hipStream_t s);
+hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32_t* row_token,
+                              const int32_t* offsets, const float* wg, const float* wu, float* a,
+                              hipStream_t s);
 hipError_t launch_down_f32(const moe_problem& p, const float* a, const int32_t* offsets,
                            const float* wd, float* yp, hipStream_t s);
 

@@ -147,7 +147,9 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, floa
  *   row_token   [T*k]     i32  token of row r for r < N; rows of an expert are
  *                              contiguous and in ascending token order (output)
  *   slot_to_row [T, k]    i32  row of slot (t, j), -1 if dropped        (output)
- *   xp          [T*k, H]  act dtype  xp[r] = x[row_token[r]] for r < N  (output)
+ *   xp          [T*k, H]  act dtype  xp[r] = x[row_token[r]] for r < N  (output), or
+ *                              NULL: the layout only, no row copy (the rows are then read
+ *                              through row_token by moe_expert_gate_up_gather)
  * All integer outputs are deterministic (no atomics-order effects).
  * --------------------------------------------------------------------------------- */
 int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
@@ -167,6 +169,10 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
  *   packed_gate_up / packed_down from moe_pack_weights.
  * moe_expert_ffn keeps `a` in the workspace; the two halves are also callable alone and
  * need no workspace (their ws / ws_bytes arguments are ignored and may be NULL / 0).
+ *
+ * moe_expert_gate_up_gather is moe_expert_gate_up with the dispatch row copy folded into
+ * the operand loads: row r of the layout is read as x[row_token[r]] (x [T, H], row_token
+ * from moe_dispatch), so xp is never materialised.  Same result, bit for bit.
  * --------------------------------------------------------------------------------- */
 int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
                    const void* packed_gate_up, const void* packed_down, void* yp, void* ws,
@@ -174,6 +180,9 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
 int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offsets,
                        const void* packed_gate_up, void* a, void* ws, size_t ws_bytes,
                        void* stream);
+int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t* row_token,
+                              const int32_t* offsets, const void* packed_gate_up, void* a,
+                              void* ws, size_t ws_bytes, void* stream);
 int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
                     const void* packed_down, void* yp, void* ws, size_t ws_bytes,
                     void* stream);
@@ -190,7 +199,8 @@ int moe_combine(const moe_problem* p, const void* yp, const float* topk_w,
                 const int32_t* slot_to_row, void* y, void* stream);
 
 /* ---------------------------------------------------------------------------------
- * moe_layer -- route, capacity, dispatch, FFN and combine in one call on one stream.
+ * moe_layer -- route, capacity, dispatch, FFN and combine in one call on one stream (the
+ * dispatch builds the layout only and gate/up gathers the token rows itself).
  * x [T, H], logits [T, E] f32, packed weights, y [T, H].  The routing outputs are
  * optional: pass NULL to keep them in the workspace, or buffers of the shapes above to
  * receive them.

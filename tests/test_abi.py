@@ -73,7 +73,10 @@ def test_workspace_and_packed_sizes(moe):
     assert p.workspace_bytes(moe.OP_DISPATCH) > 0
     ffn = p.workspace_bytes(moe.OP_FFN)
     assert ffn >= 4096 * 8 * 768 * 2  # the intermediate activation
-    assert p.workspace_bytes(moe.OP_LAYER) >= 2 * 4096 * 8 * 2048 * 2 + ffn
+    # the layer keeps yp and the intermediate activation; the rows are gathered by the
+    # gate/up kernel itself, so there is no xp in it
+    layer = p.workspace_bytes(moe.OP_LAYER)
+    assert 4096 * 8 * 2048 * 2 + ffn <= layer < 2 * 4096 * 8 * 2048 * 2 + ffn
     capped = moe.Problem(T=4096, H=2048, E=128, k=8, I=768, capacity=1024)
     assert capped.workspace_bytes(moe.OP_ROUTE) >= 4096 * 8 * 4
     assert p.packed_bytes(moe.W_GATE_UP) == 2 * 128 * 2048 * 768 * 2
@@ -93,6 +96,9 @@ def test_calls_reject_bad_arguments_before_touching_the_device(moe):
     assert st == moe.MOE_ERR_WORKSPACE
     st = moe.lib.moe_combine(ctypes.byref(c), ctypes.c_void_p(8), fake, fake, fake, None)
     assert st == moe.MOE_ERR_INVALID_ARG  # misaligned yp
+    st = moe.lib.moe_expert_gate_up_gather(ctypes.byref(c), fake, None, fake, fake, fake, None, 0,
+                                           None)
+    assert st == moe.MOE_ERR_INVALID_ARG  # gather without row_token
     bad = moe.Problem(T=64, H=100, E=8, k=2, I=128).c()
     st = moe.lib.moe_layer(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, None, None,
                            None, None, None, None, 0, None)

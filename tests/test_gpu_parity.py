@@ -251,6 +251,26 @@ def test_expert_ffn_equals_gate_up_then_down():
     assert torch.equal(yp[:N], g["yp"][:N])
 
 
+@pytest.mark.parametrize("wl", [SMALL[0], SMALL[2], SMALL[6]], ids=lambda w: w.name)
+def test_gate_up_gather_equals_gate_up_on_gathered_rows(wl):
+    """Reading the token rows through row_token (no xp) gives the xp result bit for bit,
+    for the prefill, decode and fp32 kernels; the layout-only dispatch gives the same
+    layout as the full one."""
+    m = moe()
+    p = problem_of(wl)
+    inp = synth.make_inputs(wl, DEV)
+    g = gpu_staged(p, inp)
+    d = m.dispatch(p, inp["x"], g["topk_ids"], g["keep"], rows=False)
+    a = m.expert_gate_up_gather(p, inp["x"], d["row_token"], d["offsets"], g["pgu"])
+    torch.cuda.synchronize()
+    assert d["xp"] is None
+    for name in ("counts", "offsets", "row_token", "slot_to_row"):
+        N = int(g["offsets"][-1]) if name == "row_token" else None
+        assert torch.equal(d[name][:N], g[name][:N]), name
+    N = int(g["offsets"][-1])
+    assert torch.equal(a[:N], g["a"][:N])
+
+
 def test_workspace_too_small_is_an_error():
     m = moe()
     p = m.Problem(T=64, H=128, E=8, k=2, I=64, capacity=0)
@@ -283,6 +303,11 @@ def test_full_size_workload(name):
     # every gathered row is its token's row (checked on the device, any size)
     rt = g["row_token"][:N].long()
     assert torch.equal(g["xp"][:N], inp["x"].index_select(0, rt))
+    # gate/up reading the token rows through row_token equals gate/up on xp
+    a2 = m.expert_gate_up_gather(p, inp["x"], g["row_token"], g["offsets"], g["pgu"])
+    torch.cuda.synchronize()
+    assert torch.equal(a2[:N], g["a"][:N])
+    del a2
     # the fused layer gives the same result as the staged calls
     r = m.routing_buffers(p)
     y = m.layer(p, inp["x"], inp["logits"], g["pgu"], g["pd"], routing=r)
