@@ -156,57 +156,67 @@ __device__ __forceinline__ uint64_t cap_key(const float* __restrict__ w, int32_t
   return ((uint64_t)wb << 32) | (uint32_t)(0xFFFFFFFFu - t);
 }
 
-__global__ __launch_bounds__(512) void capacity_select_kernel(
+constexpr int kCapThreads = 1024;
+constexpr int kCapLdsKeys = 12288;  // candidates whose keys are held in LDS (96 KiB)
+
+__global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
     const int32_t* __restrict__ cand_counts, const int32_t* __restrict__ cand_offsets,
     const int32_t* __restrict__ cand_slot, const float* __restrict__ w, int k, int C,
     uint8_t* __restrict__ keep) {
+  __shared__ uint64_t s_keys[kCapLdsKeys];
   __shared__ uint32_t hist[256];
-  __shared__ unsigned long long s_prefix;
-  __shared__ int s_need, s_done;
+  __shared__ int s_sel, s_need, s_done;
   const int e = blockIdx.x;
   const int cnt = cand_counts[e];
   if (cnt <= C) return;  // block-uniform
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int32_t* slots = cand_slot + cand_offsets[e];
+  // keys are built once into LDS when they fit; otherwise every pass rebuilds them
+  const bool in_lds = cnt <= kCapLdsKeys;  // block-uniform
+  if (in_lds)
+    for (int i = tid; i < cnt; i += kCapThreads) s_keys[i] = cap_key(w, slots[i], k);
+  auto key_at = [&](int i) { return in_lds ? s_keys[i] : cap_key(w, slots[i], k); };
   uint64_t prefix = 0, mask = 0;
   int need = C;
   for (int pass = 0; pass < 8; ++pass) {
     const int shift = 56 - 8 * pass;
-    for (int i = threadIdx.x; i < 256; i += blockDim.x) hist[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
-      const uint64_t key = cap_key(w, slots[i], k);
+    for (int i = tid; i < cnt; i += kCapThreads) {
+      const uint64_t key = key_at(i);
       if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t acc = 0;
-      int sel = 0;
-      for (int d = 255; d >= 0; --d) {
-        if (acc + hist[d] >= (uint32_t)need) {
-          sel = d;
-          break;
+    // The boundary digit: the largest d with (keys above d) < need <= (keys at or above d).
+    // Wavefront 0, lane l holding digits 255 - 4l .. 252 - 4l (descending).
+    if (wave == 0) {
+      uint32_t h[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[q] = hist[255 - (4 * lane + q)];
+      const int lsum = (int)(h[0] + h[1] + h[2] + h[3]);
+      int above = wave_inclusive_scan(lsum) - lsum;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above < need && above + (int)h[q] >= need) {  // exactly one lane and q
+          s_sel = 255 - (4 * lane + q);
+          s_need = need - above;
+          s_done = ((int)h[q] == need - above);
         }
-        acc += hist[d];
+        above += (int)h[q];
       }
-      need -= (int)acc;
-      prefix |= (uint64_t)sel << shift;
-      s_prefix = prefix;
-      s_need = need;
-      s_done = (hist[sel] == (uint32_t)need);
     }
     __syncthreads();
-    prefix = s_prefix;
+    const int sel = s_sel;
     need = s_need;
-    mask |= (uint64_t)0xFF << shift;
     const int done = s_done;
-    __syncthreads();
-    if (done) break;
+    prefix |= (uint64_t)sel << shift;
+    mask |= (uint64_t)0xFF << shift;
+    if (done) break;  // block-uniform
+    // (the barrier at the top of the next pass orders these reads before hist is cleared)
   }
   // keys >= prefix (the lower bits of prefix are zero) are exactly the C largest
-  for (int i = threadIdx.x; i < cnt; i += blockDim.x) {
-    const int32_t s = slots[i];
-    if (cap_key(w, s, k) < prefix) keep[s] = 0;
-  }
+  for (int i = tid; i < cnt; i += kCapThreads)
+    if (key_at(i) < prefix) keep[slots[i]] = 0;
 }
 
 // One token per block: read x[t] once, write it to each of its rows.
@@ -277,7 +287,7 @@ hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_
 hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
                                   const int32_t* cand_offsets, const int32_t* cand_slot,
                                   const float* topk_w, uint8_t* keep, hipStream_t s) {
-  hipLaunchKernelGGL(capacity_select_kernel, dim3(p.E), dim3(512), 0, s, cand_counts,
+  hipLaunchKernelGGL(capacity_select_kernel, dim3(p.E), dim3(kCapThreads), 0, s, cand_counts,
                      cand_offsets, cand_slot, topk_w, p.k, p.capacity, keep);
   return hipGetLastError();
 }

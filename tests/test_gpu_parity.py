@@ -172,6 +172,9 @@ ROUTING = [
     Workload("all_to_one_cap", T=500, H=64, E=32, k=2, I=64, capacity=100, dtype="bf16",
              logits="all_to_one", seed=26),
     Workload("cap_above_T", T=129, H=64, E=8, k=2, I=64, capacity=1000, dtype="bf16", logits="normal", seed=27),
+    # two experts with 20,000 candidates each: more keys than the selection holds in LDS
+    Workload("all_to_one_cap_big", T=20000, H=64, E=8, k=2, I=64, capacity=5000, dtype="bf16",
+             logits="all_to_one", seed=29),
     Workload("E1_k1", T=3, H=64, E=1, k=1, I=64, capacity=0, dtype="bf16", logits="normal", seed=28),
 ]
 
