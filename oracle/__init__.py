@@ -56,6 +56,19 @@ def _load():
     lib.orc_ffn_rows.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, i32]
     lib.orc_combine.restype = None
     lib.orc_combine.argtypes = [i32, P, i32, i32, P, P, P, P]
+    lib.orc_e4m3_value.restype = ctypes.c_double
+    lib.orc_e4m3_value.argtypes = [i32]
+    lib.orc_e4m3_encode.restype = i32
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_double]
+    lib.orc_ue8m0.restype = i32
+    lib.orc_ue8m0.argtypes = [ctypes.c_double]
+    for name in ("orc_e4m3_encode_vec", "orc_e4m3_value_vec", "orc_ue8m0_vec"):
+        getattr(lib, name).restype = None
+        getattr(lib, name).argtypes = [ctypes.c_int64, P, P]
+    lib.orc_quant_rows.restype = None
+    lib.orc_quant_rows.argtypes = [ctypes.c_int64, i32, i32, P, P, P]
+    lib.orc_ffn_rows_fp8.restype = None
+    lib.orc_ffn_rows_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, i32]
     _lib = lib
     return lib
 
@@ -184,3 +197,89 @@ def layer(x: np.ndarray, logits: np.ndarray, w_gate, w_up, w_down, k: int, capac
     yp, a = ffn_rows(xp, row_expert, w_gate, w_up, w_down, want_a=True, nthreads=nthreads)
     y = combine(np.arange(T, dtype=np.int32), w, lay["slot_to_row"], yp)
     return dict(topk_ids=ids, topk_w=w, keep=keep, xp=xp, a=a, yp=yp, y=y, **lay)
+
+
+# ---------------------------------------------------------------------------------------
+# FP8 (E4M3 codes with UE8M0 power-of-two block scales, blocks of 32 along the reduction
+# dimension; the readings are recorded in moe_oracle.c)
+# ---------------------------------------------------------------------------------------
+QBLOCK = 32
+
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of each E4M3 code (NaN for 0x7F / 0xFF), fp64."""
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8).ravel())
+    out = np.empty(codes.size, np.float64)
+    _load().orc_e4m3_value_vec(codes.size, _p(codes), _p(out))
+    return out
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest E4M3 code of each value (|v| <= 448), ties to even, sign kept at zero."""
+    vals = np.ascontiguousarray(np.asarray(values, dtype=np.float64).ravel())
+    out = np.empty(vals.size, np.uint8)
+    _load().orc_e4m3_encode_vec(vals.size, _p(vals), _p(out))
+    return out
+
+
+def ue8m0(amax) -> np.ndarray:
+    """E8M0 scale byte 127 + e, e the smallest integer with amax <= 448 * 2^e."""
+    vals = np.ascontiguousarray(np.asarray(amax, dtype=np.float64).ravel())
+    out = np.empty(vals.size, np.uint8)
+    _load().orc_ue8m0_vec(vals.size, _p(vals), _p(out))
+    return out
+
+
+def quant_rows(x: np.ndarray):
+    """Quantise each row of x [n, m] (m % 32 == 0; f32, bf16-as-uint16 or f64) in blocks of
+    32: returns (codes [n, m] uint8, scales [n, m / 32] uint8)."""
+    x = np.ascontiguousarray(x)
+    n, m = x.shape
+    assert m % QBLOCK == 0
+    code = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}[x.dtype]
+    codes = np.empty((n, m), np.uint8)
+    scales = np.empty((n, m // QBLOCK), np.uint8)
+    _load().orc_quant_rows(n, m, code, _p(x), _p(codes), _p(scales))
+    return codes, scales
+
+
+def quant_weights(w: np.ndarray):
+    """Quantise expert weights w [E, K, N] (K the reduction dimension) in blocks of 32 along
+    K: returns (codes [E, K, N], scales [E, K / 32, N])."""
+    E, K, N = w.shape
+    wt = np.ascontiguousarray(np.transpose(w, (0, 2, 1))).reshape(E * N, K)
+    c, s = quant_rows(wt)
+    codes = np.ascontiguousarray(np.transpose(c.reshape(E, N, K), (0, 2, 1)))
+    scales = np.ascontiguousarray(np.transpose(s.reshape(E, N, K // QBLOCK), (0, 2, 1)))
+    return codes, scales
+
+
+def dequant(codes: np.ndarray, scales: np.ndarray, axis: int) -> np.ndarray:
+    """codes * 2^(scale - 127), the scale of element i along `axis` being scales[i // 32]."""
+    v = e4m3_value(codes).reshape(codes.shape)
+    s = np.repeat(scales.astype(np.int64) - 127, QBLOCK, axis=axis)
+    return np.ldexp(v, s)
+
+
+def ffn_rows_fp8(xq, xs, row_expert, wg, wu, wd, want_a: bool = False, nthreads: int = 0):
+    """FP8 SwiGLU FFN per row.  xq/xs: quantised rows; wg, wu, wd: (codes, scales) pairs from
+    quant_weights of W_gate, W_up [E,H,I] and W_down [E,I,H].  g, u and yp accumulate in
+    fp64; a is quantised per row (blocks of 32) before the down projection.  Returns yp
+    [n,H] f64, and with want_a (a before quantisation f64, a codes, a scales)."""
+    xq = np.ascontiguousarray(xq, dtype=np.uint8)
+    xs = np.ascontiguousarray(xs, dtype=np.uint8)
+    row_expert = np.ascontiguousarray(row_expert, dtype=np.int32)
+    (gq, gs), (uq, us), (dq, ds) = [(np.ascontiguousarray(c), np.ascontiguousarray(s))
+                                    for c, s in (wg, wu, wd)]
+    n, H = xq.shape
+    E, H2, I = gq.shape
+    assert H2 == H and dq.shape == (E, I, H) and xs.shape == (n, H // QBLOCK)
+    yp = np.zeros((n, H), np.float64)
+    a = np.zeros((n, I), np.float64)
+    ac = np.zeros((n, I), np.uint8)
+    asc = np.zeros((n, I // QBLOCK), np.uint8)
+    if n:
+        _load().orc_ffn_rows_fp8(H, I, n, _p(row_expert), _p(xq), _p(xs), _p(gq), _p(gs), _p(uq),
+                                 _p(us), _p(dq), _p(ds), _p(yp), _p(a), _p(ac), _p(asc),
+                                 int(nthreads))
+    return (yp, a, ac, asc) if want_a else yp

@@ -381,3 +381,163 @@ void orc_combine(int ntok, const int32_t* tokens, int H, int k, const float* top
 void orc_exp_vec(int64_t n, const float* x, float* y) {
   for (int64_t i = 0; i < n; ++i) y[i] = orc_exp(x[i]);
 }
+
+/* ======================================================================== */
+/* FP8 expert FFN ([P4] PR body: the grouped GEMMs run in FP8 with UE8M0     */
+/* power-of-two scales, `silu_and_mul_psum_post_quant_fwd` quantises the    */
+/* SwiGLU output on the prefix-sum layout; the PR's quantisation test       */
+/* expects a scale of exactly 2^-8).  Readings recorded with the oracle:    */
+/*   - element format: OCP FP8 E4M3 (1 sign, 4 exponent bits with bias 7,   */
+/*     3 mantissa bits, subnormals, no infinities, S.1111.111 = NaN, largest */
+/*     finite 448); conversion rounds to nearest, ties to even;             */
+/*   - a scale covers a block of 32 consecutive elements along the GEMM's   */
+/*     reduction dimension and is a power of two 2^e stored as the unsigned */
+/*     E8M0 byte e + 127, e the smallest integer with amax <= 448 * 2^e     */
+/*     (nothing saturates); an all-zero block takes e = 0;                  */
+/*   - x is quantised per token row, the weights per column along the       */
+/*     reduction dimension, the SwiGLU output `a` per row before the down    */
+/*     projection; products accumulate in fp64 here.                        */
+/* ======================================================================== */
+#define ORC_QB 32
+
+/* Value of an E4M3 code (NaN for the two NaN codes). */
+double orc_e4m3_value(int code) {
+  int s = (code >> 7) & 1, E = (code >> 3) & 15, M = code & 7;
+  if (E == 15 && M == 7) return NAN;
+  double mag = (E == 0) ? ldexp((double)M, -9) : ldexp(8.0 + M, E - 10);
+  return s ? -mag : mag;
+}
+
+/* Nearest E4M3 code to v (|v| <= 448), ties to the even code; the sign is kept
+ * for values that round to zero.  Plain search over the 127 non-negative
+ * finite codes, which are increasing in value. */
+int orc_e4m3_encode(double v) {
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  int lo = 0, hi = 126; /* largest code with value <= a */
+  if (a >= 448.0) return (neg << 7) | 126;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) / 2;
+    if (orc_e4m3_value(mid) <= a) lo = mid; else hi = mid - 1;
+  }
+  int c = lo;
+  if (c < 126) {
+    double d0 = a - orc_e4m3_value(c), d1 = orc_e4m3_value(c + 1) - a;
+    if (d1 < d0 || (d1 == d0 && (c & 1))) c = c + 1;
+  }
+  return (neg << 7) | c;
+}
+
+/* E8M0 scale byte of a block with absolute maximum amax: 127 + e, e the
+ * smallest integer with amax <= 448 * 2^e (127 for amax == 0). */
+int orc_ue8m0(double amax) {
+  if (!(amax > 0.0)) return 127;
+  int e;
+  frexp(amax, &e);
+  e -= 9; /* near the answer (floor(log2 amax) - 8); the loops make it exact */
+  while (ldexp(448.0, e) < amax) ++e;
+  while (e > -127 && ldexp(448.0, e - 1) >= amax) --e;
+  if (e < -127) e = -127;
+  if (e > 127) e = 127;
+  return e + 127;
+}
+
+/* Quantise nrows rows of ncols (ncols % 32 == 0) values in blocks of 32 along
+ * each row: scales[r, b] (E8M0 bytes), codes[r, c] (E4M3).  in_dtype: 0 f32,
+ * 1 bf16, 2 f64. */
+void orc_quant_rows(int64_t nrows, int ncols, int in_dtype, const void* in, uint8_t* codes,
+                    uint8_t* scales) {
+  for (int64_t r = 0; r < nrows; ++r)
+    for (int b = 0; b < ncols / ORC_QB; ++b) {
+      double v[ORC_QB], amax = 0.0;
+      for (int i = 0; i < ORC_QB; ++i) {
+        size_t idx = (size_t)r * ncols + (size_t)b * ORC_QB + i;
+        v[i] = in_dtype == 2 ? ((const double*)in)[idx] : orc_load(in, idx, in_dtype);
+        if (fabs(v[i]) > amax) amax = fabs(v[i]);
+      }
+      int s = orc_ue8m0(amax);
+      scales[(size_t)r * (ncols / ORC_QB) + b] = (uint8_t)s;
+      for (int i = 0; i < ORC_QB; ++i)
+        codes[(size_t)r * ncols + (size_t)b * ORC_QB + i] =
+            (uint8_t)orc_e4m3_encode(ldexp(v[i], 127 - s));
+    }
+}
+
+static inline double orc_deq(const uint8_t* codes, const uint8_t* scales, size_t idx,
+                             size_t sidx) {
+  return ldexp(orc_e4m3_value(codes[idx]), (int)scales[sidx] - 127);
+}
+
+/* FP8 SwiGLU FFN of a set of rows.  Inputs are already quantised (codes +
+ * scales): rows xq/xs [nrows, H] / [nrows, H/32]; per expert the weights
+ * wg/wu [E, H, I] with scales [E, H/32, I] (blocks along H), wd [E, I, H]
+ * with scales [E, I/32, H] (blocks along I).  g and u accumulate the
+ * dequantised products in fp64; a = silu(g) * u is quantised per row in
+ * blocks of 32 (orc_quant_rows rule) and dequantised before the down
+ * projection; yp in fp64.  a_out (fp64, before quantisation), a_codes /
+ * a_scales may be NULL. */
+void orc_ffn_rows_fp8(int H, int I, int nrows, const int32_t* row_expert, const uint8_t* xq,
+                      const uint8_t* xs, const uint8_t* wgq, const uint8_t* wgs,
+                      const uint8_t* wuq, const uint8_t* wus, const uint8_t* wdq,
+                      const uint8_t* wds, double* yp, double* a_out, uint8_t* a_codes,
+                      uint8_t* a_scales, int nthreads) {
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#endif
+  const int HB = H / ORC_QB, IB = I / ORC_QB;
+#pragma omp parallel
+  {
+    double* g = (double*)malloc(sizeof(double) * (size_t)I);
+    double* u = (double*)malloc(sizeof(double) * (size_t)I);
+    double* a = (double*)malloc(sizeof(double) * (size_t)I);
+    uint8_t* aq = (uint8_t*)malloc((size_t)I);
+    uint8_t* as = (uint8_t*)malloc((size_t)IB);
+#pragma omp for schedule(dynamic, 1)
+    for (int r = 0; r < nrows; ++r) {
+      size_t e = (size_t)row_expert[r];
+      for (int i = 0; i < I; ++i) g[i] = u[i] = 0.0;
+      for (int h = 0; h < H; ++h) {
+        double xv = orc_deq(xq, xs, (size_t)r * H + h, (size_t)r * HB + h / ORC_QB);
+        for (int i = 0; i < I; ++i) {
+          size_t wi = (e * H + h) * (size_t)I + i;
+          size_t si = (e * HB + h / ORC_QB) * (size_t)I + i;
+          g[i] += xv * orc_deq(wgq, wgs, wi, si);
+          u[i] += xv * orc_deq(wuq, wus, wi, si);
+        }
+      }
+      for (int i = 0; i < I; ++i) {
+        a[i] = g[i] / (1.0 + exp(-g[i])) * u[i];
+        if (a_out) a_out[(size_t)r * I + i] = a[i];
+      }
+      orc_quant_rows(1, I, 2, a, aq, as);
+      if (a_codes) memcpy(a_codes + (size_t)r * I, aq, (size_t)I);
+      if (a_scales) memcpy(a_scales + (size_t)r * IB, as, (size_t)IB);
+      double* y = yp + (size_t)r * H;
+      for (int h = 0; h < H; ++h) y[h] = 0.0;
+      for (int i = 0; i < I; ++i) {
+        double av = orc_deq(aq, as, (size_t)i, (size_t)(i / ORC_QB));
+        for (int h = 0; h < H; ++h) {
+          size_t wi = (e * I + i) * (size_t)H + h;
+          size_t si = (e * IB + i / ORC_QB) * (size_t)H + h;
+          y[h] += av * orc_deq(wdq, wds, wi, si);
+        }
+      }
+    }
+    free(g);
+    free(u);
+    free(a);
+    free(aq);
+    free(as);
+  }
+}
+
+/* Element-wise forms of the FP8 helpers (for the pins in tests/). */
+void orc_e4m3_encode_vec(int64_t n, const double* v, uint8_t* codes) {
+  for (int64_t i = 0; i < n; ++i) codes[i] = (uint8_t)orc_e4m3_encode(v[i]);
+}
+void orc_e4m3_value_vec(int64_t n, const uint8_t* codes, double* v) {
+  for (int64_t i = 0; i < n; ++i) v[i] = orc_e4m3_value(codes[i]);
+}
+void orc_ue8m0_vec(int64_t n, const double* amax, uint8_t* bytes) {
+  for (int64_t i = 0; i < n; ++i) bytes[i] = (uint8_t)orc_ue8m0(amax[i]);
+}
