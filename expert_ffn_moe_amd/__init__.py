@@ -7,7 +7,12 @@ in the library's HIP kernels; if libmoe.so is missing or fails to load, importin
 package raises -- there is no other implementation.
 
 Call names follow the C ABI: route, dispatch, expert_gate_up, expert_gate_up_gather,
-expert_down, expert_ffn, combine, layer, plus pack_weights for the one-time weight packing.
+expert_down, expert_ffn, combine, layer, quantize_fp8, plus pack_weights for the one-time
+weight packing.
+
+Problem.dtype "fp8" means FP8 (E4M3, UE8M0 block scales) expert weights with bf16
+activations: pack_weights then takes bf16 weights and quantises them, and the intermediate
+activation `a` is a uint8 buffer of E4M3 codes followed by scale bytes (split_quantized).
 """
 from __future__ import annotations
 
@@ -22,14 +27,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16 = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
+QBLOCK = 32  # elements per UE8M0 scale
 OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER = range(5)
 W_GATE_UP, W_DOWN = 0, 1
 
 EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_packed_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
            "moe_expert_gate_up_gather",
-           "moe_expert_down", "moe_combine", "moe_layer")
+           "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8")
 
 
 class MoeError(RuntimeError):
@@ -65,6 +71,7 @@ def _load() -> ctypes.CDLL:
         "moe_expert_down": (ctypes.c_int, [PP, P, P, P, P, P, sz, P]),
         "moe_combine": (ctypes.c_int, [PP, P, P, P, P, P]),
         "moe_layer": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
+        "moe_quantize_fp8": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -90,16 +97,29 @@ class Problem:
     I: int
     capacity: int = 0
     renormalize: int = 1
-    dtype: str = "bf16"  # activations and weights: "bf16" or "f32"
+    dtype: str = "bf16"  # "bf16" or "f32" (activations and weights), "fp8" (FP8 weights)
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        """Activation dtype."""
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    @property
+    def fp8(self) -> bool:
+        return self.dtype == "fp8"
 
     def c(self) -> MoeProblem:
-        dt = MOE_BF16 if self.dtype == "bf16" else MOE_F32
+        act = MOE_F32 if self.dtype == "f32" else MOE_BF16
+        w = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8}.get(self.dtype, -1)
         return MoeProblem(self.T, self.H, self.E, self.k, self.I, self.capacity, self.renormalize,
-                          dt, dt)
+                          act, w)
+
+    def a_shape(self):
+        """Shape and dtype of the intermediate activation buffer `a`."""
+        tk = self.T * self.k
+        if self.fp8:
+            return (_align256(tk * self.I) + tk * (self.I // QBLOCK),), torch.uint8
+        return (tk, self.I), self.torch_dtype
 
     def check(self) -> int:
         c = self.c()
@@ -117,6 +137,17 @@ class Problem:
     def of(cls, wl) -> "Problem":
         """From a workload description with T, H, E, k, I, capacity, renormalize, dtype."""
         return cls(wl.T, wl.H, wl.E, wl.k, wl.I, wl.capacity, wl.renormalize, wl.dtype)
+
+
+def _align256(n: int) -> int:
+    return (n + 255) & ~255
+
+
+def split_quantized(p: Problem, a: torch.Tensor):
+    """Views of an FP8 intermediate buffer: (codes [T*k, I] u8, scales [T*k, I/32] u8)."""
+    tk = p.T * p.k
+    off = _align256(tk * p.I)
+    return a[:tk * p.I].view(tk, p.I), a[off:off + tk * (p.I // QBLOCK)].view(tk, p.I // QBLOCK)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -156,7 +187,8 @@ def workspace(p: Problem, op: int, device="cuda") -> torch.Tensor:
 
 
 def pack_weights(p: Problem, w_gate, w_up, w_down, packed_gate_up=None, packed_down=None):
-    """One-time packing of [E,H,I], [E,H,I], [E,I,H] weights into the kernels' layout."""
+    """One-time packing of [E,H,I], [E,H,I], [E,I,H] weights into the kernels' layout
+    (fp8 problems: bf16 weights, quantised while packing)."""
     dt = p.torch_dtype
     _need(w_gate, "w_gate", (p.E, p.H, p.I), dt)
     _need(w_up, "w_up", (p.E, p.H, p.I), dt)
@@ -217,7 +249,8 @@ def expert_gate_up(p: Problem, xp, offsets, packed_gate_up, out=None, ws=None):
     tk = p.T * p.k
     _need(xp, "xp", (tk, p.H), dt)
     _need(offsets, "offsets", (p.E + 1,), torch.int32)
-    a = _empty((tk, p.I), dt, xp.device) if out is None else out
+    a = _empty(*p.a_shape(), xp.device) if out is None else out
+    _need(a, "a", *p.a_shape())
     ws = workspace(p, OP_FFN, xp.device) if ws is None else ws
     c = p.c()
     _call("moe_expert_gate_up", ctypes.byref(c), _ptr(xp), _ptr(offsets), _ptr(packed_gate_up),
@@ -232,10 +265,13 @@ def expert_gate_up_gather(p: Problem, x, row_token, offsets, packed_gate_up, out
     _need(x, "x", (p.T, p.H), dt)
     _need(row_token, "row_token", (tk,), torch.int32)
     _need(offsets, "offsets", (p.E + 1,), torch.int32)
-    a = _empty((tk, p.I), dt, x.device) if out is None else out
+    a = _empty(*p.a_shape(), x.device) if out is None else out
+    _need(a, "a", *p.a_shape())
+    if ws is None and p.fp8:
+        ws = workspace(p, OP_FFN, x.device)
     c = p.c()
     _call("moe_expert_gate_up_gather", ctypes.byref(c), _ptr(x), _ptr(row_token), _ptr(offsets),
-          _ptr(packed_gate_up), _ptr(a), None, 0, _stream())
+          _ptr(packed_gate_up), _ptr(a), _ptr(ws), 0 if ws is None else ws.numel(), _stream())
     return a
 
 
@@ -243,7 +279,7 @@ def expert_down(p: Problem, a, offsets, packed_down, out=None, ws=None):
     """yp = a Wd per expert segment; returns yp [T*k, H]."""
     dt = p.torch_dtype
     tk = p.T * p.k
-    _need(a, "a", (tk, p.I), dt)
+    _need(a, "a", *p.a_shape())
     _need(offsets, "offsets", (p.E + 1,), torch.int32)
     yp = _empty((tk, p.H), dt, a.device) if out is None else out
     ws = workspace(p, OP_FFN, a.device) if ws is None else ws
@@ -295,6 +331,22 @@ def layer(p: Problem, x, logits, packed_gate_up, packed_down, out=None, routing=
           _ptr(r.get("counts")), _ptr(r.get("offsets")), _ptr(r.get("row_token")),
           _ptr(r.get("slot_to_row")), _ptr(ws), ws.numel(), _stream())
     return y
+
+
+def quantize_fp8(x, codes=None, scales=None):
+    """Per-row FP8 quantisation of bf16 x [rows, cols] (cols a multiple of 32): returns
+    (codes [rows, cols] u8 E4M3, scales [rows, cols/32] u8 UE8M0)."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    rows, cols = x.shape
+    _need(x, "x", (rows, cols), torch.bfloat16)
+    codes = _empty((rows, cols), torch.uint8, x.device) if codes is None else codes
+    scales = _empty((rows, cols // QBLOCK), torch.uint8, x.device) if scales is None else scales
+    _need(codes, "codes", (rows, cols), torch.uint8)
+    _need(scales, "scales", (rows, cols // QBLOCK), torch.uint8)
+    _call("moe_quantize_fp8", _ptr(x), ctypes.c_int64(rows), ctypes.c_int32(cols), _ptr(codes),
+          _ptr(scales), _stream())
+    return codes, scales
 
 
 def routing_buffers(p: Problem, device="cuda"):

@@ -41,29 +41,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f +
 
 constexpr int kOperandElems = 512;  // one packed 32x16 (or 16x32) operand block
 
-// ------------------------------------------------------------------------------------
-// Prefill grouped GEMM: persistent, one block of 4 wavefronts per CU.
-//
-// Work item = (M tile of up to 256 rows of one expert, N group).  Wavefront w computes
-// all rows of the tile for 2 operand columns (64 GEMM columns):
-//   GATE_UP: the gate and the up column of 32 outputs of `a` -> block: 128 columns of a
-//   DOWN   : 64 columns of yp                               -> block: 256 columns of yp
-// 8 x 2 accumulators of 32x32 (256 fp32 per lane, in AGPRs); 32-row fragments past the
-// expert's last row are skipped, so a ragged tile costs at most 31 idle rows.
-//
-// K runs in k-steps of 16 (one MFMA) grouped in stages of two.  Weight operands come
-// straight from memory into a ring of 8 k-steps of registers (refilled as soon as a
-// k-step's MFMAs are issued).  The 256x32 activation stage goes through LDS (double
-// buffer, operand order, one contiguous 1 KiB fragment per wavefront store) and is
-// loaded into registers 3 stages ahead.  Every wait therefore covers loads issued at
-// least 3 stages earlier, although vector-memory counters complete in issue order.
-//
-// Scheduling: every block first turns `offsets` into per-expert M-tile starts (LDS).  The
-// M tiles are split into 8 contiguous ranges, one per XCD (workgroups are dispatched to
-// XCDs round-robin, so block b runs on XCD b % 8); the blocks of an XCD take its work
-// items in turn.  Items of one expert therefore run together on one XCD, and the weight
-// and activation bytes they share are served by that XCD's L2.
-// ------------------------------------------------------------------------------------
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
 constexpr int kWaves = 8;               // wavefronts per block (two per SIMD)

@@ -26,20 +26,37 @@ using namespace moe;
 
 namespace {
 
-size_t elem_bytes(int dt) { return dt == MOE_BF16 ? 2 : 4; }
+size_t elem_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }  // activations: bf16 unless f32
+
+bool is_fp8(const moe_problem& p) { return p.w_dtype == MOE_FP8; }
+
+// Quantised activation rows: E4M3 codes [rows, cols] then UE8M0 scale bytes [rows, cols/32]
+// at the next 256-byte boundary.
+size_t q_rows_bytes(size_t rows, size_t cols) { return align256(rows * cols) + rows * (cols / 32); }
+uint8_t* q_scales(void* q, size_t rows, size_t cols) {
+  return static_cast<uint8_t*>(q) + align256(rows * cols);
+}
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15) == 0; }
 
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Workspace of the FFN: the intermediate activation (moe_expert_ffn and moe_layer only;
-// the split calls take it as an argument and need no workspace).
+// Workspace of the FFN: the intermediate activation (moe_expert_ffn and moe_layer; the
+// split calls take it as an argument), and for FP8 problems the quantised input rows
+// (needed by every gate/up call).
 struct FfnScratch {
   void* a;
+  void* xq;  // FP8: codes + scales of up to T*k input rows
 };
 FfnScratch carve_ffn(Carve& c, const moe_problem& p) {
   FfnScratch f{};
-  f.a = c.take<char>((size_t)p.T * p.k * p.I * elem_bytes(p.act_dtype));
+  const size_t tk = (size_t)p.T * p.k;
+  if (is_fp8(p)) {
+    f.a = c.take<char>(q_rows_bytes(tk, p.I));
+    f.xq = c.take<char>(q_rows_bytes(tk, p.H));
+  } else {
+    f.a = c.take<char>(tk * p.I * elem_bytes(p.act_dtype));
+  }
   return f;
 }
 
@@ -129,8 +146,22 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
 }
 
 // Gate/up over the layout: rows xs[r], or token rows xs[row_token[r]] if row_token != NULL.
+// FP8: the input rows (T token rows, or T*k rows of xp) are quantised into f.xq first.
 hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_token,
-                       const int32_t* offsets, const void* pgu, void* a, hipStream_t s) {
+                       const int32_t* offsets, const void* pgu, void* a, const FfnScratch& f,
+                       hipStream_t s) {
+  if (is_fp8(p)) {
+    const size_t tk = (size_t)p.T * p.k;
+    const size_t rows = row_token ? (size_t)p.T : tk;
+    uint8_t* xq = static_cast<uint8_t*>(f.xq);
+    uint8_t* xsc = q_scales(f.xq, tk, p.H);
+    // layout rows: only the N = offsets[E] filled ones
+    hipError_t err = launch_quant_rows(xs, (int64_t)rows, p.H, row_token ? nullptr : offsets + p.E,
+                                       xq, xsc, s);
+    if (err != hipSuccess) return err;
+    return launch_gate_up_fp8(p, xq, xsc, row_token, offsets, pgu, static_cast<uint8_t*>(a),
+                              q_scales(a, tk, p.I), s);
+  }
   if (p.act_dtype == MOE_F32) {
     const size_t n = (size_t)p.E * p.H * p.I;
     return launch_gate_up_f32(p, (const float*)xs, row_token, offsets, (const float*)pgu,
@@ -141,6 +172,11 @@ hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
                     const void* pd, void* yp, hipStream_t s) {
+  if (is_fp8(p)) {
+    const size_t tk = (size_t)p.T * p.k;
+    return launch_down_fp8(p, static_cast<const uint8_t*>(a),
+                           q_scales(const_cast<void*>(a), tk, p.I), offsets, pd, yp, s);
+  }
   if (p.act_dtype == MOE_F32)
     return launch_down_f32(p, (const float*)a, offsets, (const float*)pd, (float*)yp, s);
   return launch_down_bf16(p, a, offsets, pd, yp, s);
@@ -166,11 +202,16 @@ int moe_problem_check(const moe_problem* p) {
   if (p->T < 1 || p->H < 1 || p->E < 1 || p->k < 1 || p->I < 1) return MOE_ERR_INVALID_ARG;
   if (p->k > p->E) return MOE_ERR_INVALID_ARG;
   if ((p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) ||
-      (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16))
+      (p->w_dtype != MOE_F32 && p->w_dtype != MOE_BF16 && p->w_dtype != MOE_FP8))
     return MOE_ERR_INVALID_ARG;
   if (p->renormalize != 0 && p->renormalize != 1) return MOE_ERR_INVALID_ARG;
   if (p->E > kMaxE || p->k > 32) return MOE_ERR_UNSUPPORTED;
-  if (p->act_dtype != p->w_dtype) return MOE_ERR_UNSUPPORTED;
+  if (p->w_dtype == MOE_FP8) {
+    // FP8 weights take bf16 activations; a stage of the FP8 GEMM is 128 elements of K
+    if (p->act_dtype != MOE_BF16 || p->H % 128 || p->I % 128) return MOE_ERR_UNSUPPORTED;
+  } else if (p->act_dtype != p->w_dtype) {
+    return MOE_ERR_UNSUPPORTED;
+  }
   const int mult = p->act_dtype == MOE_BF16 ? 64 : 8;
   if (p->H % mult || p->I % mult) return MOE_ERR_UNSUPPORTED;
   if ((int64_t)p->T * p->k >= ((int64_t)1 << 31) - 2 * (int64_t)kPrefillBM * 1024)
@@ -185,6 +226,15 @@ size_t moe_workspace_bytes(const moe_problem* p, int op) {
 
 size_t moe_packed_bytes(const moe_problem* p, int which) {
   if (moe_problem_check(p) != MOE_OK) return 0;
+  if (p->w_dtype == MOE_FP8) {
+    if (which == MOE_W_GATE_UP)
+      return align256(fp8_packed_code_bytes(p->E, p->H, p->I, 2)) +
+             fp8_packed_scale_bytes(p->E, p->H, p->I, 2);
+    if (which == MOE_W_DOWN)
+      return align256(fp8_packed_code_bytes(p->E, p->I, p->H, 1)) +
+             fp8_packed_scale_bytes(p->E, p->I, p->H, 1);
+    return 0;
+  }
   const size_t n = (size_t)p->E * p->H * p->I * elem_bytes(p->w_dtype);
   if (which == MOE_W_GATE_UP) return 2 * n;
   if (which == MOE_W_DOWN) return n;
@@ -199,6 +249,9 @@ int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
   if (!w_gate || !w_up || !w_down || !packed_gate_up || !packed_down)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(packed_gate_up) || !aligned16(packed_down)) return MOE_ERR_INVALID_ARG;
+  if (p->w_dtype == MOE_FP8)
+    return status_of(launch_pack_fp8(*p, w_gate, w_up, w_down, packed_gate_up, packed_down,
+                                     as_stream(stream)));
   return status_of(
       launch_pack(*p, w_gate, w_up, w_down, packed_gate_up, packed_down, as_stream(stream)));
 }
@@ -236,9 +289,14 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
   if (st != MOE_OK) return st;
   if (!xp || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
   if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
-  (void)ws;
-  (void)ws_bytes;
-  return status_of(run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, as_stream(stream)));
+  FfnScratch f{};
+  if (is_fp8(*p)) {  // the quantised input rows live in the workspace
+    if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+    Carve c(ws);
+    f = carve_ffn(c, *p);
+  }
+  return status_of(
+      run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, f, as_stream(stream)));
 }
 
 int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t* row_token,
@@ -248,10 +306,22 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
   if (st != MOE_OK) return st;
   if (!x || !row_token || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
-  (void)ws;
-  (void)ws_bytes;
+  FfnScratch f{};
+  if (is_fp8(*p)) {
+    if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
+    Carve c(ws);
+    f = carve_ffn(c, *p);
+  }
   return status_of(
-      run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, as_stream(stream)));
+      run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, f, as_stream(stream)));
+}
+
+int moe_quantize_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
+                     void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  return status_of(launch_quant_rows(x, rows, cols, nullptr, codes, scales, as_stream(stream)));
 }
 
 int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
@@ -279,7 +349,7 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   Carve c(ws);
   FfnScratch f = carve_ffn(c, *p);
   hipStream_t s = as_stream(stream);
-  hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, s);
+  hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, f, s);
   if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, s);
   return status_of(err);
 }
@@ -320,7 +390,7 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
                        row_token, slot_to_row, nullptr, L.rank, s);
   if (err == hipSuccess)
-    err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, s);
+    err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, L.ffn, s);
   if (err == hipSuccess) err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, s);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, y, s);
   return status_of(err);

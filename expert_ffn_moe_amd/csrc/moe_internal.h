@@ -17,6 +17,7 @@ constexpr int kMaxE = 1024;
 constexpr int kPrefillBM = 128;
 
 __host__ __device__ inline int div_up(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t div_up64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 // Bump allocator over a caller-provided workspace (sizes are rounded to 256 bytes).
@@ -90,5 +91,23 @@ hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32
                               hipStream_t s);
 hipError_t launch_down_f32(const moe_problem& p, const float* a, const int32_t* offsets,
                            const float* wd, float* yp, hipStream_t s);
+
+// ---- quant_fp8.hip / ffn_fp8.hip (FP8 E4M3 operands, UE8M0 scales per 32 along K)
+size_t fp8_packed_code_bytes(int E, int K, int N, int nmat);
+size_t fp8_packed_scale_bytes(int E, int K, int N, int nmat);
+hipError_t launch_pack_fp8(const moe_problem& p, const void* wg, const void* wu, const void* wd,
+                           void* packed_gu, void* packed_d, hipStream_t s);
+// bf16 rows [rows, K] -> codes [rows, K], scales [rows, K / 32]; rows >= *row_limit
+// skipped if row_limit is not NULL (a device pointer).
+hipError_t launch_quant_rows(const void* in, int64_t rows, int K, const int32_t* row_limit,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Gate/up on quantised rows (xq/xs; token rows through row_token if not NULL) -> the
+// quantised intermediate (aq [rows, I], as [rows, I / 32]); down -> yp (bf16).
+hipError_t launch_gate_up_fp8(const moe_problem& p, const uint8_t* xq, const uint8_t* xs,
+                              const int32_t* row_token, const int32_t* offsets,
+                              const void* packed_gu, uint8_t* aq, uint8_t* as, hipStream_t s);
+hipError_t launch_down_fp8(const moe_problem& p, const uint8_t* aq, const uint8_t* as,
+                           const int32_t* offsets, const void* packed_d, void* yp,
+                           hipStream_t s);
 
 }  // namespace moe

@@ -58,7 +58,15 @@ typedef enum {
   MOE_ERR_HIP = 4
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_FP8 (weights only, with bf16 activations): [LightLLM] walkthrough table row
+ * "Grouped MoE kernel support" (FP8 grouped GEMMs over the prefix-sum layout, SwiGLU
+ * fused with quantisation, UE8M0 scale tests) and the review comment on the UE8M0 test
+ * (block scales are exact powers of two, 2^-8 in its case).  Format: OCP E4M3 codes
+ * (largest finite 448, round to nearest even, saturating) with one UE8M0 scale byte
+ * (value 2^(byte-127)) per 32 consecutive elements along the reduction dimension; the
+ * scale of a block is the smallest power of two 2^e with max|x| <= 448 * 2^e (2^0 for an
+ * all-zero block). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8 = 2 } moe_dtype;
 
 /* Problem description.  T tokens of width H, E experts, top-k, SwiGLU width I. */
 typedef struct {
@@ -69,14 +77,15 @@ typedef struct {
   /* 1: the top-k weights are renormalised to sum to 1 ([LightLLM] `norm_topk_prob`);
    * 0: they are the plain softmax probabilities over all E experts. */
   int32_t renormalize;
-  int32_t act_dtype; /* moe_dtype of x, xp, the intermediate activation, yp, y */
-  int32_t w_dtype;   /* moe_dtype of the expert weights */
+  int32_t act_dtype; /* moe_dtype of x, xp, yp, y and (unless w_dtype is FP8) of the
+                        intermediate activation */
+  int32_t w_dtype;   /* moe_dtype of the expert weights (MOE_FP8 needs act MOE_BF16) */
 } moe_problem;
 
 typedef enum {
   MOE_OP_ROUTE = 0,
   MOE_OP_DISPATCH = 1,
-  MOE_OP_FFN = 2, /* moe_expert_ffn (moe_expert_gate_up / moe_expert_down need none) */
+  MOE_OP_FFN = 2, /* moe_expert_ffn; FP8 problems: also moe_expert_gate_up(_gather) */
   MOE_OP_COMBINE = 3,
   MOE_OP_LAYER = 4
 } moe_op;
@@ -89,8 +98,9 @@ const char* moe_status_str(int status);
 /* Host-only validation of a problem ([axolotl] `validate_expert_parallel_topology`:
  * layouts the kernels do not handle are rejected up front, never run another way).
  * Returns MOE_OK, MOE_ERR_INVALID_ARG (p NULL, T/H/E/k/I < 1, k > E, dtype unknown) or
- * MOE_ERR_UNSUPPORTED: E > 1024, k > 32, act_dtype != w_dtype, H or I not a multiple
- * of 64 (bf16) or 8 (f32), T*k >= 2^31. */
+ * MOE_ERR_UNSUPPORTED: E > 1024, k > 32, act_dtype != w_dtype (except FP8 weights with
+ * bf16 activations), H or I not a multiple of 64 (bf16), 128 (FP8) or 8 (f32),
+ * T*k >= 2^31. */
 int moe_problem_check(const moe_problem* p);
 
 /* Workspace bytes that `op` needs for problem p (0 if p is invalid). */
@@ -109,6 +119,11 @@ size_t moe_workspace_bytes(const moe_problem* p, int op);
  * moe_pack_weights: writes packed_gate_up (E*2*H*I elements) and packed_down
  *   (E*I*H elements) from the natural layout; elements are copied bit for bit.
  *   For f32 problems the packed layout is the natural layout.
+ *   For FP8 problems the natural layout is bf16 and packing quantises: every block of
+ *   32 elements along the reduction dimension (H for gate/up, I for down) of one output
+ *   column gets its UE8M0 scale and E4M3 codes, as moe_quantize_fp8 would compute for
+ *   that column; the packed buffer holds the codes in matrix-core operand order followed
+ *   (at a 256-byte boundary) by the scale bytes.
  * --------------------------------------------------------------------------------- */
 size_t moe_packed_bytes(const moe_problem* p, int which);
 int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
@@ -173,6 +188,14 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
  * moe_expert_gate_up_gather is moe_expert_gate_up with the dispatch row copy folded into
  * the operand loads: row r of the layout is read as x[row_token[r]] (x [T, H], row_token
  * from moe_dispatch), so xp is never materialised.  Same result, bit for bit.
+ *
+ * FP8 weights (w_dtype MOE_FP8): the bf16 input rows are first quantised per row as by
+ * moe_quantize_fp8 (into the workspace: these calls then need ws of
+ * moe_workspace_bytes(p, MOE_OP_FFN) bytes), the products use the E4M3 codes scaled by
+ * their UE8M0 block scales with fp32 accumulation, and the intermediate activation `a` is
+ * stored quantised the same way: E4M3 codes [T*k, I] (row r at a + r*I) followed, at the
+ * next 256-byte boundary, by the scale bytes [T*k, I/32].  Its size is
+ * align256(T*k*I) + T*k*I/32 bytes.  yp stays bf16.
  * --------------------------------------------------------------------------------- */
 int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
                    const void* packed_gate_up, const void* packed_down, void* yp, void* ws,
@@ -186,6 +209,18 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
 int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
                     const void* packed_down, void* yp, void* ws, size_t ws_bytes,
                     void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_quantize_fp8 -- the per-block activation quantisation of the FP8 path (same
+ * passages as MOE_FP8): for each row of x [rows, cols] bf16 and each block b of 32
+ * columns, scales[row, b] = the UE8M0 byte of the block and codes[row, c] = the E4M3
+ * code of x[row, c] / 2^(scale-127), rounded to nearest even, saturating at 448.
+ *   codes [rows, cols] u8 (16-byte aligned), scales [rows, cols/32] u8.
+ * rows = 0 enqueues nothing.  MOE_ERR_INVALID_ARG: rows < 0, cols not a positive
+ * multiple of 32, NULL or misaligned pointers.
+ * --------------------------------------------------------------------------------- */
+int moe_quantize_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes,
+                     uint8_t* scales, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_combine -- [LightLLM] walkthrough, "Synchronous prefill and decode execution":

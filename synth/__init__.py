@@ -11,6 +11,8 @@ Distributions (readings of the workload descriptions, documented with the tests)
   * W_gate, W_up: [E, H, I]; W_down: [E, I, H]; N(0, sigma = 1/sqrt(fan_in)) with
     fan_in = H for gate/up and I for down.
   * bf16 tensors are drawn in fp32 and rounded to bf16 (round to nearest even).
+  * "fp8" workloads draw the same bf16 tensors; the FP8 weights are their quantisation
+    (done by the path under test and, separately, by the oracle).
 """
 from __future__ import annotations
 
@@ -22,6 +24,7 @@ import torch
 
 F32 = "f32"
 BF16 = "bf16"
+FP8 = "fp8"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -33,7 +36,7 @@ class Workload:
     k: int
     I: int
     capacity: int  # <= 0: no cap
-    dtype: str  # activation and weight dtype: "f32" or "bf16"
+    dtype: str  # "f32" or "bf16" (activations and weights), "fp8" (bf16 activations)
     logits: str  # recipe name, see make_logits
     seed: int
     renormalize: int = 1
@@ -41,7 +44,7 @@ class Workload:
 
     @property
     def torch_dtype(self) -> torch.dtype:
-        return torch.float32 if self.dtype == F32 else torch.bfloat16
+        return torch.float32 if self.dtype == F32 else torch.bfloat16  # activations
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -65,6 +68,9 @@ WORKLOADS: Dict[str, Workload] = {
                             dtype=BF16, logits="normal", seed=5,
                             note="DeepSeek-V3-shaped decode batch, weight-streaming bound"),
 }
+# The bf16 layer shapes with FP8 expert weights (same seeds, so the same bf16 draws).
+for _n in ("qwen3_30b_a3b", "glm_skew_cap", "dsv3_prefill", "dsv3_decode"):
+    WORKLOADS[_n + "_fp8"] = WORKLOADS[_n].replace(name=_n + "_fp8", dtype=FP8)
 
 
 def _gen(device, seed: int, stream: int) -> torch.Generator:

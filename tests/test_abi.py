@@ -14,7 +14,7 @@ HEADER = os.path.join(ROOT, "include", "moe.h")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -103,3 +103,38 @@ def test_calls_reject_bad_arguments_before_touching_the_device(moe):
     st = moe.lib.moe_layer(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, None, None,
                            None, None, None, None, 0, None)
     assert st == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_fp8_problem_check_and_sizes(moe):
+    # FP8 weights go with bf16 activations and need H, I multiples of 128
+    assert moe.Problem(64, 256, 8, 2, 384, dtype="fp8").check() == 0
+    assert moe.Problem(64, 192, 8, 2, 384, dtype="fp8").check() == moe.MOE_ERR_UNSUPPORTED
+    assert moe.Problem(64, 256, 8, 2, 320, dtype="fp8").check() == moe.MOE_ERR_UNSUPPORTED
+    c = moe.Problem(64, 256, 8, 2, 384, dtype="fp8").c()
+    c.act_dtype = moe.MOE_F32
+    assert moe.lib.moe_problem_check(ctypes.byref(c)) == moe.MOE_ERR_UNSUPPORTED
+    c.act_dtype = moe.MOE_FP8  # FP8 is a weight format only
+    assert moe.lib.moe_problem_check(ctypes.byref(c)) == moe.MOE_ERR_INVALID_ARG
+    p = moe.Problem(T=4096, H=2048, E=128, k=8, I=768, dtype="fp8")
+    align = lambda n: (n + 255) & ~255
+    # codes (one byte per weight) then one scale byte per 32 along K, grouped 4 k-steps of
+    # 64 per 4-byte word
+    gu_codes = 128 * 2 * 2048 * 768
+    assert p.packed_bytes(moe.W_GATE_UP) == align(gu_codes) + 128 * (768 // 32) * 2 * 8 * 256
+    assert p.packed_bytes(moe.W_DOWN) == align(128 * 768 * 2048) + 128 * (2048 // 32) * 3 * 256
+    # the FFN workspace holds the quantised intermediate and the quantised input rows
+    tk = 4096 * 8
+    q = lambda cols: align(tk * cols) + tk * cols // 32
+    assert p.workspace_bytes(moe.OP_FFN) == align(q(768)) + align(q(2048))
+    assert p.a_shape() == ((q(768),), moe.torch.uint8)
+
+
+def test_quantize_fp8_rejects_bad_arguments(moe):
+    fake = ctypes.c_void_p(256)
+    q = moe.lib.moe_quantize_fp8
+    assert q(fake, ctypes.c_int64(4), ctypes.c_int32(48), fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(fake, ctypes.c_int64(-1), ctypes.c_int32(64), fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(None, ctypes.c_int64(4), ctypes.c_int32(64), fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(8), ctypes.c_int64(4), ctypes.c_int32(64), fake, fake,
+             None) == moe.MOE_ERR_INVALID_ARG
+    assert q(None, ctypes.c_int64(0), ctypes.c_int32(64), None, None, None) == moe.MOE_OK
