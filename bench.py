@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/sec on 1 MI355X; % bf16 MFMA peak (GEMM), % HBM peak (dispatch)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
-PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3}  # dense MFMA bf16; fp32 vector
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA bf16, fp8; fp32 vector
 DEFAULT_WORKLOAD = "qwen3_30b_a3b"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -52,18 +52,22 @@ def parse():
 
 
 def algorithmic(wl, N, E_hit):
-    """Per-launch algorithmic HBM bytes and flops of each stage (decimal units): every input
-    read once and every output written once."""
-    b = 2 if wl.dtype == "bf16" else 4
+    """Per-stage algorithmic HBM bytes and flops (decimal units): every input read once and
+    every output written once.  FP8 weights and the FP8 intermediate count one byte per
+    element plus one scale byte per 32; the FP8 gate/up stage starts from the bf16 token
+    rows (its per-row quantisation is part of the stage)."""
+    b = 4 if wl.dtype == "f32" else 2                       # activations
+    wb = 1 + 1 / 32 if wl.dtype == "fp8" else b             # weights
+    ab = 1 + 1 / 32 if wl.dtype == "fp8" else b             # intermediate a
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     return {
         "route": dict(bytes=T * E * 4 + T * k * 9, flops=0),
         # ids (+ keep) in; counts, offsets, row_token, slot_to_row out
         "dispatch": dict(bytes=T * k * 5 + N * 4 + T * k * 4 + E * 8, flops=0),
         # weights of the experts hit, the token rows x (once) and row_token in; a out
-        "gate_up": dict(bytes=E_hit * 2 * H * I * b + T * H * b + N * 4 + N * I * b,
+        "gate_up": dict(bytes=E_hit * 2 * H * I * wb + T * H * b + N * 4 + N * I * ab,
                         flops=4 * N * H * I),
-        "down": dict(bytes=E_hit * I * H * b + N * I * b + N * H * b, flops=2 * N * H * I),
+        "down": dict(bytes=E_hit * I * H * wb + N * I * ab + N * H * b, flops=2 * N * H * I),
         "combine": dict(bytes=N * H * b + T * k * 8 + T * H * b, flops=0),
     }
 
@@ -74,7 +78,7 @@ def roofline_of(stage, alg, sec, dtype):
     t_mfma = a["flops"] / (PEAK_TFLOPS[dtype] * 1e12) if a["flops"] else 0.0
     if t_mfma > t_hbm:
         ach = a["flops"] / sec / 1e12
-        return dict(bound="mfma" if dtype == "bf16" else "alu", achieved=round(ach, 2),
+        return dict(bound="alu" if dtype == "f32" else "mfma", achieved=round(ach, 2),
                     peak=PEAK_TFLOPS[dtype], unit="TFLOP/s", frac=round(ach / PEAK_TFLOPS[dtype], 4))
     ach = a["bytes"] / sec / 1e9
     return dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM_GBS, unit="GB/s",
@@ -113,6 +117,9 @@ def cpu_baseline(wl, inp, target_s):
     threads = min(16, len(os.sched_getaffinity(0)))
     host = {n: (synth.bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy())
             for n, t in inp.items()}
+    fp8 = wl.dtype == "fp8"
+    if fp8:  # weight quantisation is the one-time packing step: outside the timed part
+        wq = [oracle.quant_weights(host[n]) for n in ("w_gate", "w_up", "w_down")]
     t0 = time.perf_counter()
     ids, w = oracle.route(host["logits"], wl.k, wl.renormalize)
     keep = oracle.capacity(ids, w, wl.E, wl.capacity)
@@ -126,7 +133,12 @@ def cpu_baseline(wl, inp, target_s):
         rexp = (np.searchsorted(lay["offsets"], rows, side="right") - 1).astype(np.int32)
         xrows = host["x"][lay["row_token"][rows]]
         t1 = time.perf_counter()
-        yp = oracle.ffn_rows(xrows, rexp, host["w_gate"], host["w_up"], host["w_down"], nthreads=threads)
+        if fp8:
+            xq, xs = oracle.quant_rows(xrows)
+            yp = oracle.ffn_rows_fp8(xq, xs, rexp, *wq, nthreads=threads)
+        else:
+            yp = oracle.ffn_rows(xrows, rexp, host["w_gate"], host["w_up"], host["w_down"],
+                                 nthreads=threads)
         pos = {int(r): i for i, r in enumerate(rows)}
         s2r = np.array([[pos.get(int(r), -1) for r in lay["slot_to_row"][t]] for t in tokens], np.int32)
         oracle.combine(np.arange(len(tokens), dtype=np.int32), w[tokens], s2r, yp)
@@ -182,7 +194,8 @@ def main():
                 offsets=torch.empty(wl.E + 1, dtype=torch.int32, device=dev),
                 row_token=torch.empty(tk, dtype=torch.int32, device=dev),
                 slot_to_row=torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev), xp=None)
-    a = torch.empty(tk, wl.I, dtype=dt, device=dev)
+    a_shape, a_dtype = p.a_shape()
+    a = torch.empty(a_shape, dtype=a_dtype, device=dev)
     yp = torch.empty(tk, wl.H, dtype=dt, device=dev)
     y = torch.empty(wl.T, wl.H, dtype=dt, device=dev)
     stages = ["route", "dispatch", "gate_up", "down", "combine"]
@@ -197,7 +210,8 @@ def main():
         moe.dispatch(p, inp["x"], ids, keep if wl.capacity > 0 else None, out=disp,
                      ws=ws[moe.OP_DISPATCH], rows=False)
         mark(2)
-        moe.expert_gate_up_gather(p, inp["x"], disp["row_token"], disp["offsets"], pgu, out=a)
+        moe.expert_gate_up_gather(p, inp["x"], disp["row_token"], disp["offsets"], pgu, out=a,
+                                  ws=ws[moe.OP_FFN] if p.fp8 else None)
         mark(3)
         moe.expert_down(p, a, disp["offsets"], pd, out=yp, ws=ws[moe.OP_FFN])
         mark(4)
