@@ -67,6 +67,10 @@ def _load():
         getattr(lib, name).argtypes = [ctypes.c_int64, P, P]
     lib.orc_quant_rows.restype = None
     lib.orc_quant_rows.argtypes = [ctypes.c_int64, i32, i32, P, P, P]
+    lib.orc_route_grouped.restype = None
+    lib.orc_route_grouped.argtypes = [i32, i32, i32, i32, i32, i32, P, P, P]
+    lib.orc_router_logits.restype = None
+    lib.orc_router_logits.argtypes = [i32, i32, i32, i32, P, P, P]
     lib.orc_ffn_rows_fp8.restype = None
     lib.orc_ffn_rows_fp8.argtypes = [i32, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P, i32]
     _lib = lib
@@ -111,6 +115,35 @@ def route(logits: np.ndarray, k: int, renormalize: int = 1):
     w = np.empty((T, k), np.float32)
     _load().orc_route(T, E, k, int(renormalize), _p(logits), _p(ids), _p(w))
     return ids, w
+
+
+def route_grouped(logits: np.ndarray, k: int, n_group: int, topk_group: int,
+                  renormalize: int = 1):
+    """Group-limited top-k (groups of E / n_group consecutive experts, group score = its
+    largest logit, the topk_group best groups, then top-k inside them): ids, weights."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    if n_group < 1 or E % n_group or not (1 <= topk_group <= n_group):
+        raise ValueError("need E % n_group == 0 and 1 <= topk_group <= n_group")
+    if not (1 <= k <= min(topk_group * (E // n_group), 64)):
+        raise ValueError("need 1 <= k <= min(topk_group * E / n_group, 64)")
+    ids = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float32)
+    _load().orc_route_grouped(T, E, k, int(renormalize), n_group, topk_group, _p(logits),
+                              _p(ids), _p(w))
+    return ids, w
+
+
+def router_logits(x: np.ndarray, w_router: np.ndarray) -> np.ndarray:
+    """logits [T, E] f64 = x [T, H] times W_r [E, H] transposed (f32, or bf16 as uint16)."""
+    x = np.ascontiguousarray(x)
+    w_router = np.ascontiguousarray(w_router)
+    assert x.dtype == w_router.dtype and x.shape[1] == w_router.shape[1]
+    T, H = x.shape
+    E = w_router.shape[0]
+    out = np.empty((T, E), np.float64)
+    _load().orc_router_logits(T, H, E, _dtype_code(x), _p(x), _p(w_router), _p(out))
+    return out
 
 
 def capacity(ids: np.ndarray, w: np.ndarray, E: int, C: int) -> np.ndarray:

@@ -153,6 +153,97 @@ void orc_route(int T, int E, int k, int renormalize, const float* logits,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Group-limited selection.  [P4] call-order paragraph: `experts()` keeps   */
+/* doing grouped top-k inside the layer for some models; the pages do not   */
+/* give the group rule.  Reading (the plainest one):                        */
+/*   - the E experts form n_group equal groups of consecutive ids;          */
+/*   - a group's score is the largest logit in it;                          */
+/*   - the topk_group groups with the largest scores are taken, ties to     */
+/*     the lower group index;                                               */
+/*   - the k largest logits among the experts of the taken groups are       */
+/*     selected (slot order: logit descending, ties to the lower id).       */
+/* Weights exactly as in orc_route: with renormalisation over the k chosen  */
+/* (m, the largest chosen logit, is the largest logit overall: its group    */
+/* always has the top score); without, the plain softmax over all E.        */
+/* n_group = 1 is orc_route.                                                */
+/* ------------------------------------------------------------------------ */
+void orc_route_grouped(int T, int E, int k, int renormalize, int n_group, int topk_group,
+                       const float* logits, int32_t* topk_ids, float* topk_w) {
+  const int gs = E / n_group;
+  unsigned char* allowed = (unsigned char*)malloc((size_t)E);
+  unsigned char* gtaken = (unsigned char*)malloc((size_t)n_group);
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (size_t)t * E;
+    /* group scores, then the topk_group best groups */
+    memset(gtaken, 0, (size_t)n_group);
+    memset(allowed, 0, (size_t)E);
+    for (int r = 0; r < topk_group; ++r) {
+      int bg = -1;
+      float bs = 0.0f;
+      for (int g = 0; g < n_group; ++g) {
+        if (gtaken[g]) continue;
+        float sc = l[g * gs];
+        for (int e = g * gs + 1; e < (g + 1) * gs; ++e)
+          if (l[e] > sc) sc = l[e];
+        if (bg < 0 || sc > bs) { bg = g; bs = sc; } /* strict: ties keep the lower g */
+      }
+      gtaken[bg] = 1;
+      for (int e = bg * gs; e < (bg + 1) * gs; ++e) allowed[e] = 1;
+    }
+    /* top-k among the allowed experts */
+    memset(taken, 0, (size_t)E);
+    int32_t* ids = topk_ids + (size_t)t * k;
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (!allowed[e] || taken[e]) continue;
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      taken[best] = 1;
+      ids[j] = best;
+    }
+    /* weights */
+    float m = l[ids[0]];
+    float ex[64];
+    float s = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      ex[j] = orc_exp(l[ids[j]] - m);
+      s = s + ex[j];
+    }
+    if (!renormalize) {
+      s = 0.0f;
+      for (int e = 0; e < E; ++e) s = s + orc_exp(l[e] - m);
+    }
+    for (int j = 0; j < k; ++j) topk_w[(size_t)t * k + j] = ex[j] / s;
+  }
+  free(allowed);
+  free(gtaken);
+  free(taken);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router logits.  [P4] call-order paragraph: the layer's own `experts()`   */
+/* path computes the routing from the hidden states (the gate); the plain   */
+/* reading is a linear gate without bias: logits[t, e] = sum_h x[t, h] *    */
+/* W_r[e, h], W_r stored [E, H] (one row of H weights per expert).  fp64    */
+/* accumulation, h ascending.                                               */
+/* ------------------------------------------------------------------------ */
+static inline double orc_load(const void* p, size_t i, int dtype);
+
+void orc_router_logits(int T, int H, int E, int dtype, const void* x, const void* w_router,
+                       double* logits) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int h = 0; h < H; ++h)
+        acc += orc_load(x, (size_t)t * H + h, dtype) * orc_load(w_router, (size_t)e * H + h, dtype);
+      logits[(size_t)t * E + e] = acc;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Per-expert capacity.  [P1] `expert_token_capacity` row: at most C        */
 /* (token, expert) assignments per expert per forward; the lowest-weight    */
 /* excess ones are dropped.  Order: weight descending, ties to the lower    */
