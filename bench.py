@@ -42,6 +42,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--router", action="store_true",
+                    help="route from the hidden states: router GEMM x W_r^T + selection "
+                         "(moe_router; DeepSeek-V3-style 8/4 expert groups when E = 256) instead "
+                         "of moe_route on given logits")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -51,7 +55,7 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic(wl, N, E_hit):
+def algorithmic(wl, N, E_hit, router=False):
     """Per-stage algorithmic HBM bytes and flops (decimal units): every input read once and
     every output written once.  FP8 weights and the FP8 intermediate count one byte per
     element plus one scale byte per 32; the FP8 gate/up stage starts from the bf16 token
@@ -61,7 +65,9 @@ def algorithmic(wl, N, E_hit):
     ab = 1 + 1 / 32 if wl.dtype == "fp8" else b             # intermediate a
     T, H, E, k, I = wl.T, wl.H, wl.E, wl.k, wl.I
     return {
-        "route": dict(bytes=T * E * 4 + T * k * 9, flops=0),
+        # with the router: x and W_r in (bf16), ids/weights/keep out; else logits in
+        "route": (dict(bytes=T * H * 2 + E * H * 2 + T * k * 9, flops=2 * T * H * E) if router
+                  else dict(bytes=T * E * 4 + T * k * 9, flops=0)),
         # ids (+ keep) in; counts, offsets, row_token, slot_to_row out
         "dispatch": dict(bytes=T * k * 5 + N * 4 + T * k * 4 + E * 8, flops=0),
         # weights of the experts hit, the token rows x (once) and row_token in; a out
@@ -74,6 +80,8 @@ def algorithmic(wl, N, E_hit):
 
 def roofline_of(stage, alg, sec, dtype):
     a = alg[stage]
+    if stage == "route":
+        dtype = "bf16"  # the router GEMM runs in bf16 whatever the expert weights
     t_hbm = a["bytes"] / (PEAK_HBM_GBS * 1e9)
     t_mfma = a["flops"] / (PEAK_TFLOPS[dtype] * 1e12) if a["flops"] else 0.0
     if t_mfma > t_hbm:
@@ -104,7 +112,7 @@ def measured_traffic(workload, stage):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, inp, target_s):
+def cpu_baseline(wl, inp, target_s, wr=None, groups=(1, 1)):
     """The oracle (as it stands) on a bounded sample: routing, capacity and layout over all
     T tokens, the FFN and combine over a sample of tokens; scaled to tokens/s."""
     import numpy as np
@@ -121,7 +129,11 @@ def cpu_baseline(wl, inp, target_s):
     if fp8:  # weight quantisation is the one-time packing step: outside the timed part
         wq = [oracle.quant_weights(host[n]) for n in ("w_gate", "w_up", "w_down")]
     t0 = time.perf_counter()
-    ids, w = oracle.route(host["logits"], wl.k, wl.renormalize)
+    if wr is not None:  # router front-end: fp64 logits from x and W_r, then the selection
+        lg = oracle.router_logits(host["x"], synth.bf16_bits(wr)).astype(np.float32)
+        ids, w = oracle.route_grouped(lg, wl.k, groups[0], groups[1], wl.renormalize)
+    else:
+        ids, w = oracle.route(host["logits"], wl.k, wl.renormalize)
     keep = oracle.capacity(ids, w, wl.E, wl.capacity)
     lay = oracle.layout(ids, keep, wl.E)
     t_route = time.perf_counter() - t0
@@ -186,7 +198,8 @@ def main():
     tk = wl.T * wl.k
     dt = p.torch_dtype
     # every buffer allocated once, outside the timed region
-    ws = {op: moe.workspace(p, op, dev) for op in (moe.OP_ROUTE, moe.OP_DISPATCH, moe.OP_FFN)}
+    ws = {op: moe.workspace(p, op, dev)
+          for op in (moe.OP_ROUTE, moe.OP_DISPATCH, moe.OP_FFN, moe.OP_ROUTER)}
     routing = (torch.empty(wl.T, wl.k, dtype=torch.int32, device=dev),
                torch.empty(wl.T, wl.k, dtype=torch.float32, device=dev),
                torch.empty(wl.T, wl.k, dtype=torch.uint8, device=dev))
@@ -199,13 +212,19 @@ def main():
     yp = torch.empty(tk, wl.H, dtype=dt, device=dev)
     y = torch.empty(wl.T, wl.H, dtype=dt, device=dev)
     stages = ["route", "dispatch", "gate_up", "down", "combine"]
+    groups = (8, 4) if wl.E == 256 else (1, 1)
+    wr = synth.make_router_weights(wl, dev) if args.router else None
 
     def step(ev=None):
         def mark(i):
             if ev is not None:
                 ev[i].record()
         mark(0)
-        ids, w, keep = moe.route(p, inp["logits"], out=routing, ws=ws[moe.OP_ROUTE])
+        if wr is not None:
+            ids, w, keep, _ = moe.router(p, inp["x"], wr, *groups, out=routing,
+                                         ws=ws[moe.OP_ROUTER])
+        else:
+            ids, w, keep = moe.route(p, inp["logits"], out=routing, ws=ws[moe.OP_ROUTE])
         mark(1)
         moe.dispatch(p, inp["x"], ids, keep if wl.capacity > 0 else None, out=disp,
                      ws=ws[moe.OP_DISPATCH], rows=False)
@@ -237,7 +256,7 @@ def main():
 
     N = int(disp["offsets"][-1].item())
     E_hit = int((disp["counts"] > 0).sum().item())
-    alg = algorithmic(wl, N, E_hit)
+    alg = algorithmic(wl, N, E_hit, router=args.router)
     dom = max(("gate_up", "down", "dispatch", "combine", "route"), key=lambda s: stage_ms[s])
     roof = roofline_of(dom, alg, stage_ms[dom] / 1e3, wl.dtype)
     roof["kernel"] = dom
@@ -250,12 +269,12 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded; routing logits and weights drawn per the workload recipe)",
-        "config": {"workload": wl.name, "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
+        "config": {"workload": wl.name + ("+router" if args.router else ""), "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
                    "capacity": wl.capacity, "N_kept": N, "experts_hit": E_hit},
         "roofline": roof, "stages": per_stage,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, wr, groups)
     print(json.dumps(out), flush=True)
 
 

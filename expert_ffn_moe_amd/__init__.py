@@ -29,13 +29,14 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 QBLOCK = 32  # elements per UE8M0 scale
-OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER = range(5)
+OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER, OP_ROUTER = range(6)
 W_GATE_UP, W_DOWN = 0, 1
 
 EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_packed_bytes",
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
            "moe_expert_gate_up_gather",
-           "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8")
+           "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
+           "moe_route_grouped", "moe_router")
 
 
 class MoeError(RuntimeError):
@@ -72,6 +73,10 @@ def _load() -> ctypes.CDLL:
         "moe_combine": (ctypes.c_int, [PP, P, P, P, P, P]),
         "moe_layer": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P]),
         "moe_quantize_fp8": (ctypes.c_int, [P, ctypes.c_int64, ctypes.c_int32, P, P, P]),
+        "moe_route_grouped": (ctypes.c_int, [PP, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P,
+                                             sz, P]),
+        "moe_router": (ctypes.c_int, [PP, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
+                                      sz, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -216,6 +221,43 @@ def route(p: Problem, logits, out=None, ws=None):
     _call("moe_route", ctypes.byref(c), _ptr(logits), _ptr(ids), _ptr(w), _ptr(keep), _ptr(ws),
           ws.numel(), _stream())
     return ids, w, keep
+
+
+def route_grouped(p: Problem, logits, n_group: int, topk_group: int, out=None, ws=None):
+    """Group-limited top-k + capacity: returns (topk_ids, topk_w, keep) as route()."""
+    _need(logits, "logits", (p.T, p.E), torch.float32)
+    dev = logits.device
+    ids, w, keep = out if out is not None else (
+        _empty((p.T, p.k), torch.int32, dev), _empty((p.T, p.k), torch.float32, dev),
+        _empty((p.T, p.k), torch.uint8, dev))
+    ws = workspace(p, OP_ROUTE, dev) if ws is None else ws
+    c = p.c()
+    _call("moe_route_grouped", ctypes.byref(c), _ptr(logits), ctypes.c_int32(n_group),
+          ctypes.c_int32(topk_group), _ptr(ids), _ptr(w), _ptr(keep), _ptr(ws), ws.numel(),
+          _stream())
+    return ids, w, keep
+
+
+def router(p: Problem, x, w_router, n_group: int = 1, topk_group: int = 1, logits=None,
+           want_logits: bool = False, out=None, ws=None):
+    """Router GEMM (logits = x W_r^T, W_r [E, H]) + (grouped) top-k + capacity.  Returns
+    (topk_ids, topk_w, keep, logits) -- logits None unless asked for (or passed in)."""
+    _need(x, "x", (p.T, p.H), torch.bfloat16)
+    _need(w_router, "w_router", (p.E, p.H), torch.bfloat16)
+    dev = x.device
+    if logits is None and want_logits:
+        logits = _empty((p.T, p.E), torch.float32, dev)
+    if logits is not None:
+        _need(logits, "logits", (p.T, p.E), torch.float32)
+    ids, w, keep = out if out is not None else (
+        _empty((p.T, p.k), torch.int32, dev), _empty((p.T, p.k), torch.float32, dev),
+        _empty((p.T, p.k), torch.uint8, dev))
+    ws = workspace(p, OP_ROUTER, dev) if ws is None else ws
+    c = p.c()
+    _call("moe_router", ctypes.byref(c), _ptr(x), _ptr(w_router), ctypes.c_int32(n_group),
+          ctypes.c_int32(topk_group), _ptr(logits), _ptr(ids), _ptr(w), _ptr(keep), _ptr(ws),
+          ws.numel(), _stream())
+    return ids, w, keep, logits
 
 
 def dispatch(p: Problem, x, topk_ids, keep=None, out=None, ws=None, rows=True):

@@ -85,11 +85,33 @@ LayerScratch carve_layer(Carve& c, const moe_problem& p) {
   return L;
 }
 
+// Routing scratch: the capacity pipeline's, only with a cap.
+RankScratch carve_route(Carve& c, const moe_problem& p) {
+  return p.capacity > 0 ? carve_rank(c, p, true) : RankScratch{};
+}
+
+// Router scratch: the split-K partial logit planes, then the routing scratch.
+struct RouterScratch {
+  float* part;
+  RankScratch rank;
+};
+RouterScratch carve_router(Carve& c, const moe_problem& p) {
+  RouterScratch r{};
+  r.part = c.take<float>((size_t)router_plan(p).split * p.T * p.E);
+  r.rank = carve_route(c, p);
+  return r;
+}
+
+// Every entry point carves its workspace with the same function that sizes it here.
 size_t ws_bytes_of(const moe_problem& p, int op) {
   Carve c(nullptr);
   switch (op) {
     case MOE_OP_ROUTE:
-      if (p.capacity > 0) carve_rank(c, p, true);
+      carve_route(c, p);
+      break;
+    case MOE_OP_ROUTER:
+      if (!router_supported(p)) return 0;
+      carve_router(c, p);
       break;
     case MOE_OP_DISPATCH:
       carve_rank(c, p, false);
@@ -118,11 +140,11 @@ int check_ws(const moe_problem* p, int op, const void* ws, size_t ws_bytes) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
-// The routing pipeline: top-k, then (with a cap) candidate layout + radix select.
-hipError_t run_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
-                     uint8_t* keep, const RankScratch& r, hipStream_t s) {
-  hipError_t err = launch_route(p, logits, ids, w, keep, s);
-  if (err != hipSuccess || p.capacity <= 0) return err;
+// Capacity after the selection: candidate layout + radix select (no-op without a cap).
+hipError_t run_capacity(const moe_problem& p, int32_t* ids, float* w, uint8_t* keep,
+                        const RankScratch& r, hipStream_t s) {
+  hipError_t err = hipSuccess;
+  if (p.capacity <= 0) return err;
   if ((err = launch_chunk_hist(p, ids, nullptr, r.chunk_hist, s)) != hipSuccess) return err;
   if ((err = launch_scan(p, r.chunk_hist, r.chunk_base, r.cand_counts, s)) != hipSuccess)
     return err;
@@ -130,6 +152,20 @@ hipError_t run_route(const moe_problem& p, const float* logits, int32_t* ids, fl
                             nullptr, nullptr, r.cand_slot, s)) != hipSuccess)
     return err;
   return launch_capacity_select(p, r.cand_counts, r.cand_offsets, r.cand_slot, w, keep, s);
+}
+
+// The routing pipeline: top-k (group-limited if asked), then the capacity.
+hipError_t run_route(const moe_problem& p, const float* logits, int n_group, int topk_group,
+                     int32_t* ids, float* w, uint8_t* keep, const RankScratch& r,
+                     hipStream_t s) {
+  hipError_t err = launch_route(p, logits, n_group, topk_group, ids, w, keep, s);
+  return err != hipSuccess ? err : run_capacity(p, ids, w, keep, r, s);
+}
+
+// 1 <= topk_group <= n_group <= 64, n_group divides E, k fits in the taken groups.
+bool groups_ok(const moe_problem& p, int n_group, int topk_group) {
+  return n_group >= 1 && n_group <= 64 && p.E % n_group == 0 && topk_group >= 1 &&
+         topk_group <= n_group && (int64_t)topk_group * (p.E / n_group) >= p.k;
 }
 
 hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
@@ -263,8 +299,44 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, floa
   if (!logits || !topk_ids || !topk_w || !keep) return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
-  RankScratch r = carve_rank(c, *p, p->capacity > 0);
-  return status_of(run_route(*p, logits, topk_ids, topk_w, keep, r, as_stream(stream)));
+  RankScratch r = carve_route(c, *p);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
+  return status_of(run_route(*p, logits, 1, 1, topk_ids, topk_w, keep, r, as_stream(stream)));
+}
+
+int moe_route_grouped(const moe_problem* p, const float* logits, int32_t n_group,
+                      int32_t topk_group, int32_t* topk_ids, float* topk_w, uint8_t* keep,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!logits || !topk_ids || !topk_w || !keep || !groups_ok(*p, n_group, topk_group))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  RankScratch r = carve_route(c, *p);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
+  return status_of(run_route(*p, logits, n_group, topk_group, topk_ids, topk_w, keep, r,
+                             as_stream(stream)));
+}
+
+int moe_router(const moe_problem* p, const void* x, const void* w_router, int32_t n_group,
+               int32_t topk_group, float* logits, int32_t* topk_ids, float* topk_w,
+               uint8_t* keep, void* ws, size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!x || !w_router || !topk_ids || !topk_w || !keep || !groups_ok(*p, n_group, topk_group))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
+  if (!router_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if ((st = check_ws(p, MOE_OP_ROUTER, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  RouterScratch r = carve_router(c, *p);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;
+  hipStream_t s = as_stream(stream);
+  hipError_t err = launch_router(*p, x, w_router, n_group, topk_group, r.part, logits, topk_ids,
+                                 topk_w, keep, s);
+  if (err == hipSuccess) err = run_capacity(*p, topk_ids, topk_w, keep, r.rank, s);
+  return status_of(err);
 }
 
 int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
@@ -278,6 +350,7 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
   if ((st = check_ws(p, MOE_OP_DISPATCH, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   RankScratch r = carve_rank(c, *p, false);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   return status_of(run_dispatch(*p, x, topk_ids, keep, counts, offsets, row_token, slot_to_row,
                                 xp, r, as_stream(stream)));
 }
@@ -294,6 +367,7 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
     if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
     Carve c(ws);
     f = carve_ffn(c, *p);
+    if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   }
   return status_of(
       run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, f, as_stream(stream)));
@@ -311,6 +385,7 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
     if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
     Carve c(ws);
     f = carve_ffn(c, *p);
+    if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   }
   return status_of(
       run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, f, as_stream(stream)));
@@ -348,6 +423,7 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   FfnScratch f = carve_ffn(c, *p);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   hipStream_t s = as_stream(stream);
   hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, f, s);
   if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, s);
@@ -376,6 +452,7 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if ((st = check_ws(p, MOE_OP_LAYER, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   LayerScratch L = carve_layer(c, *p);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   if (!topk_ids) topk_ids = L.ids;
   if (!topk_w) topk_w = L.w;
   if (!keep) keep = L.keep;
@@ -384,7 +461,7 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if (!row_token) row_token = L.row_token;
   if (!slot_to_row) slot_to_row = L.slot_to_row;
   hipStream_t s = as_stream(stream);
-  hipError_t err = run_route(*p, logits, topk_ids, topk_w, keep, L.rank, s);
+  hipError_t err = run_route(*p, logits, 1, 1, topk_ids, topk_w, keep, L.rank, s);
   // dispatch builds the layout only: gate/up reads the token rows through row_token
   if (err == hipSuccess)
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,

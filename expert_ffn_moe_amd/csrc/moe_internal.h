@@ -44,8 +44,21 @@ struct RankScratch {
 RankScratch carve_rank(Carve& c, const moe_problem& p, bool with_capacity);
 
 // ---- route.hip
-hipError_t launch_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
-                        uint8_t* keep, hipStream_t s);
+// Top-k (group-limited when 1 < n_group and topk_group < n_group) from fp32 logits.
+hipError_t launch_route(const moe_problem& p, const float* logits, int n_group, int topk_group,
+                        int32_t* ids, float* w, uint8_t* keep, hipStream_t s);
+// Router front-end: logits = x W_r^T (bf16, W_r [E, H]) as `split` partial planes
+// [split][T][E] f32 in `part` (rows per block, split of H chosen by router_plan), then the
+// selection of their in-order sum; the summed logits are also written if not NULL.
+struct RouterPlan {
+  int rows;   // tokens per block: 64, 128 or 256
+  int split;  // slices of H (a divisor of H / 64)
+};
+bool router_supported(const moe_problem& p);
+RouterPlan router_plan(const moe_problem& p);
+hipError_t launch_router(const moe_problem& p, const void* x, const void* wr, int n_group,
+                         int topk_group, float* part, float* logits, int32_t* ids, float* w,
+                         uint8_t* keep, hipStream_t s);
 
 // ---- dispatch.hip
 // Per-chunk histogram of (kept) assignments per expert.

@@ -1,5 +1,6 @@
 // Top-k routing (LightLLM PR #1687, call-order paragraph: top-k in the logical expert
-// space, `norm_topk_prob` renormalisation).  One wavefront per token.
+// space, `norm_topk_prob` renormalisation, grouped top-k inside `experts()`).  One
+// wavefront per token.
 //
 // Selection: each lane holds the logits of experts lane, lane+64, ...; k rounds of a
 // wavefront max over 64-bit keys (order-preserving logit bits << 32 | ~expert) pick the
@@ -50,29 +51,40 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-template <int EPL>  // experts per lane: E <= 64 * EPL
-__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int T,
-                                                    int E, int k, int renorm,
-                                                    int32_t* __restrict__ ids,
-                                                    float* __restrict__ w,
-                                                    uint8_t* __restrict__ keep) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // wave-uniform
-  const float* row = logits + (size_t)t * E;
-
+// Selection and weights of one token whose logits the wavefront holds (lane: experts
+// lane, lane + 64, ...; lv[i] ignored for lane + 64 i >= E).  Group limit (n_group > 1 and
+// topk_group < n_group): groups of gs = E / n_group consecutive experts; topk_group rounds
+// of a wavefront max over the keys of experts in groups not yet taken pick the groups in
+// order of their best logit (ties: the lower expert id, hence the lower group); experts
+// outside the taken groups are then removed before the k selection rounds.
+template <int EPL>
+__device__ __forceinline__ void select_token(const float (&lv)[EPL], int E, int k, int renorm,
+                                             int n_group, int topk_group, int lane, size_t o,
+                                             int32_t* __restrict__ ids, float* __restrict__ w,
+                                             uint8_t* __restrict__ keep) {
   uint64_t key[EPL];
-  float lv[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = lane + 64 * i;
-    if (e < E) {
-      lv[i] = row[e];
-      key[i] = ((uint64_t)ordered_bits(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
-    } else {
-      lv[i] = 0.0f;
-      key[i] = 0;  // below every real key
+    key[i] = e < E ? ((uint64_t)ordered_bits(lv[i]) << 32) | (uint32_t)(~(uint32_t)e) : 0;
+  }
+  if (n_group > 1 && topk_group < n_group) {  // wave-uniform
+    const int gs = E / n_group;
+    int grp[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) grp[i] = (lane + 64 * i) / gs;
+    uint64_t taken = 0;  // bit g: group g taken (n_group <= 64)
+    for (int r = 0; r < topk_group; ++r) {
+      uint64_t best = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!((taken >> grp[i]) & 1)) best = max_u64(best, key[i]);
+      best = wave_max_u64(best);
+      taken |= (uint64_t)1 << ((int)(~(uint32_t)best) / gs);
     }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (!((taken >> grp[i]) & 1)) key[i] = 0;
   }
 
   uint64_t mine = 0;  // lane j ends with the key chosen in round j
@@ -105,31 +117,244 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     }
   }
   if (lane < k) {
-    const size_t o = (size_t)t * k + lane;
-    ids[o] = e;
-    w[o] = ex / s;
-    keep[o] = 1;
+    ids[o + lane] = e;
+    w[o + lane] = ex / s;
+    keep[o + lane] = 1;
   }
 }
 
+// One wavefront per token.  The logits are the sum, in plane order, of S fp32 planes
+// (S = 1: the logits themselves; S > 1: the router GEMM's split-K partial sums), written
+// to logits_out if it is not NULL, then selected.
+template <int EPL>  // experts per lane: E <= 64 * EPL
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits, int S,
+                                                    size_t plane, int T, int E, int k,
+                                                    int renorm, int n_group, int topk_group,
+                                                    float* __restrict__ logits_out,
+                                                    int32_t* __restrict__ ids,
+                                                    float* __restrict__ w,
+                                                    uint8_t* __restrict__ keep) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform
+  const float* row = logits + (size_t)t * E;
+  float lv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    float v = 0.0f;
+    if (e < E) {
+      v = row[e];
+#pragma unroll 8
+      for (int q = 1; q < S; ++q) v = v + row[q * plane + e];
+      if (logits_out) logits_out[(size_t)t * E + e] = v;
+    }
+    lv[i] = v;
+  }
+  select_token<EPL>(lv, E, k, renorm, n_group, topk_group, lane, (size_t)t * k, ids, w, keep);
+}
+
 template <int EPL>
-hipError_t launch_route_t(const moe_problem& p, const float* logits, int32_t* ids, float* w,
+hipError_t launch_route_t(const moe_problem& p, const float* logits, int S, int n_group,
+                          int topk_group, float* logits_out, int32_t* ids, float* w,
                           uint8_t* keep, hipStream_t s) {
   dim3 grid(div_up(p.T, 4));
-  hipLaunchKernelGGL(route_kernel<EPL>, grid, dim3(256), 0, s, logits, p.T, p.E, p.k,
-                     p.renormalize, ids, w, keep);
+  hipLaunchKernelGGL(route_kernel<EPL>, grid, dim3(256), 0, s, logits, S,
+                     (size_t)p.T * p.E, p.T, p.E, p.k, p.renormalize, n_group, topk_group,
+                     logits_out, ids, w, keep);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const moe_problem& p, const float* logits, int S, int n_group,
+                         int topk_group, float* logits_out, int32_t* ids, float* w,
+                         uint8_t* keep, hipStream_t s) {
+  if (p.E <= 64)
+    return launch_route_t<1>(p, logits, S, n_group, topk_group, logits_out, ids, w, keep, s);
+  if (p.E <= 128)
+    return launch_route_t<2>(p, logits, S, n_group, topk_group, logits_out, ids, w, keep, s);
+  if (p.E <= 256)
+    return launch_route_t<4>(p, logits, S, n_group, topk_group, logits_out, ids, w, keep, s);
+  if (p.E <= 512)
+    return launch_route_t<8>(p, logits, S, n_group, topk_group, logits_out, ids, w, keep, s);
+  return launch_route_t<16>(p, logits, S, n_group, topk_group, logits_out, ids, w, keep, s);
+}
+
+// ---------------------------------------------------------------------------------------
+// Router front-end: logits = x W_r^T (bf16 operands, fp32 accumulation on the matrix
+// cores), split along H into S slices so that the grid fills the chip whatever T is; the
+// selection kernel above sums the S partial planes in order before selecting (so the
+// split-K reduction and the selection are one launch).
+//
+// A block takes R = 16 W rows (W wavefronts) and all E <= 256 experts for one slice of H:
+// wavefront w computes its 16 rows against every expert with v_mfma_f32_16x16x32_bf16
+// (E / 16 accumulators of 4 registers).  Its x rows stream straight from memory, one chunk
+// of 64 ahead (no other wavefront needs them); the gate weights, shared by all wavefronts,
+// go through LDS in chunks of 64 along H (E rows x 128 bytes, 16-byte pieces swizzled by
+// (e >> 1) & 7 so that the 16 rows of one read touch every bank once), double-buffered
+// with the next chunk held in registers.
+// ---------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kRouterMaxE = 256;
+
+__device__ __forceinline__ int wr_slot(int e, int piece) { return e * 8 + (piece ^ ((e >> 1) & 7)); }
+
+template <int NT, int W>  // E = 16 NT experts, W wavefronts (16 W rows)
+__global__ __launch_bounds__(64 * W) void router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ wr,
+                                                             int T, int H, int cps,
+                                                             float* __restrict__ part) {
+  constexpr int E = 16 * NT;
+  constexpr int kPieces = E * 8;                        // 16-byte pieces per chunk
+  constexpr int kPer = (kPieces + 64 * W - 1) / (64 * W);  // per thread
+  __shared__ uint4 lds[2 * E * 8];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int row0 = blockIdx.x * 16 * W;
+  const int c0 = blockIdx.y * cps;  // first chunk of this slice
+  const int ar = min(row0 + 16 * wave + (lane & 15), T - 1);
+  const uint16_t* ap = x + (size_t)ar * H + 64 * c0 + 8 * (lane >> 4);
+  const uint16_t* wp = wr + 64 * c0;
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{};
+  uint4 pre[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + 64 * W * j;
+    if (q < kPieces) pre[j] = *(const uint4*)(wp + (size_t)(q >> 3) * H + 8 * (q & 7));
+  }
+  // x chunks c, c + 1, c + 2 in registers (HBM latency spans a few chunks of MFMAs)
+  uint4 xa[3][2];
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    const int cd = min(d, cps - 1);
+    xa[d][0] = *(const uint4*)(ap + 64 * cd);
+    xa[d][1] = *(const uint4*)(ap + 64 * cd + 32);
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int q = tid + 64 * W * j;
+    if (q < kPieces) lds[wr_slot(q >> 3, q & 7)] = pre[j];
+  }
+  __syncthreads();
+  for (int c = 0; c < cps; ++c) {
+    const int buf = c & 1;
+    const int cn = min(c + 1, cps - 1);  // the last iteration reloads its own chunk
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + 64 * W * j;
+      if (q < kPieces) pre[j] = *(const uint4*)(wp + (size_t)(q >> 3) * H + 64 * cn + 8 * (q & 7));
+    }
+    const int c3 = min(c + 3, cps - 1);
+    const uint4 n0 = *(const uint4*)(ap + 64 * c3);
+    const uint4 n1 = *(const uint4*)(ap + 64 * c3 + 32);
+    const uint4* b = lds + buf * (E * 8);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[0][ks]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint4 bv = b[wr_slot(16 * t + (lane & 15), 4 * ks + (lane >> 4))];
+        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv),
+                                                          acc[t], 0, 0, 0);
+      }
+    }
+    uint4* nb = lds + (buf ^ 1) * (E * 8);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int q = tid + 64 * W * j;
+      if (q < kPieces) nb[wr_slot(q >> 3, q & 7)] = pre[j];
+    }
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      xa[d][0] = xa[d + 1][0];
+      xa[d][1] = xa[d + 1][1];
+    }
+    xa[2][0] = n0;
+    xa[2][1] = n1;
+    __syncthreads();
+  }
+  // partial logits of this slice: accumulator element i of lane l is row
+  // 4 (l / 16) + i of the wavefront's 16, expert 16 t + l % 16
+  float* out = part + (size_t)blockIdx.y * T * E;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + 16 * wave + 4 * (lane >> 4) + i;
+    if (r < T) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) out[(size_t)r * E + 16 * t + (lane & 15)] = acc[t][i];
+    }
+  }
+}
+
+template <int NT>
+hipError_t launch_router_gemm_t(const moe_problem& p, const RouterPlan& plan, const void* x,
+                                const void* wr, float* part, hipStream_t s) {
+  const dim3 grid(div_up(p.T, plan.rows), plan.split);
+  const int cps = p.H / 64 / plan.split;
+  if (plan.rows == 256)
+    hipLaunchKernelGGL((router_gemm_kernel<NT, 16>), grid, dim3(1024), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, p.T, p.H, cps, part);
+  else if (plan.rows == 128)
+    hipLaunchKernelGGL((router_gemm_kernel<NT, 8>), grid, dim3(512), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, p.T, p.H, cps, part);
+  else
+    hipLaunchKernelGGL((router_gemm_kernel<NT, 4>), grid, dim3(256), 0, s,
+                       (const uint16_t*)x, (const uint16_t*)wr, p.T, p.H, cps, part);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const moe_problem& p, const float* logits, int32_t* ids, float* w,
-                        uint8_t* keep, hipStream_t s) {
-  if (p.E <= 64) return launch_route_t<1>(p, logits, ids, w, keep, s);
-  if (p.E <= 128) return launch_route_t<2>(p, logits, ids, w, keep, s);
-  if (p.E <= 256) return launch_route_t<4>(p, logits, ids, w, keep, s);
-  if (p.E <= 512) return launch_route_t<8>(p, logits, ids, w, keep, s);
-  return launch_route_t<16>(p, logits, ids, w, keep, s);
+hipError_t launch_route(const moe_problem& p, const float* logits, int n_group, int topk_group,
+                        int32_t* ids, float* w, uint8_t* keep, hipStream_t s) {
+  return launch_select(p, logits, 1, n_group, topk_group, nullptr, ids, w, keep, s);
+}
+
+bool router_supported(const moe_problem& p) {
+  return p.act_dtype == MOE_BF16 && p.E % 16 == 0 && p.E <= kRouterMaxE && p.H % 64 == 0;
+}
+
+// Rows per block, then the smallest split of the H / 64 chunks (a divisor, so slices are
+// equal) that gives at least 256 blocks; at most 16 slices (the selection kernel reads
+// every partial plane).
+RouterPlan router_plan(const moe_problem& p) {
+  RouterPlan plan;
+  plan.rows = p.T >= 8192 ? 256 : (p.T >= 2048 ? 128 : 64);
+  const int tiles = div_up(p.T, plan.rows);
+  const int nch = p.H / 64;
+  plan.split = 1;
+  for (int d = 1; d <= nch && d <= 16; ++d) {
+    if (nch % d) continue;
+    plan.split = d;
+    if ((int64_t)tiles * d >= 256) break;
+  }
+  return plan;
+}
+
+hipError_t launch_router(const moe_problem& p, const void* x, const void* wr, int n_group,
+                         int topk_group, float* part, float* logits, int32_t* ids, float* w,
+                         uint8_t* keep, hipStream_t s) {
+  const RouterPlan plan = router_plan(p);
+  hipError_t err;
+  switch (p.E / 16) {
+#define MOE_ROUTER_CASE(n) \
+  case n:                  \
+    err = launch_router_gemm_t<n>(p, plan, x, wr, part, s); \
+    break;
+    MOE_ROUTER_CASE(1) MOE_ROUTER_CASE(2) MOE_ROUTER_CASE(3) MOE_ROUTER_CASE(4)
+    MOE_ROUTER_CASE(5) MOE_ROUTER_CASE(6) MOE_ROUTER_CASE(7) MOE_ROUTER_CASE(8)
+    MOE_ROUTER_CASE(9) MOE_ROUTER_CASE(10) MOE_ROUTER_CASE(11) MOE_ROUTER_CASE(12)
+    MOE_ROUTER_CASE(13) MOE_ROUTER_CASE(14) MOE_ROUTER_CASE(15) MOE_ROUTER_CASE(16)
+#undef MOE_ROUTER_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  if (err != hipSuccess) return err;
+  return launch_select(p, part, plan.split, n_group, topk_group, logits, ids, w, keep, s);
 }
 
 }  // namespace moe

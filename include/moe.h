@@ -3,6 +3,7 @@
  * expert-parallel mixture-of-experts layer.
  *
  *   moe_route        top-k routing + per-expert capacity           (route)
+ *   moe_router       router GEMM from the hidden states + grouped top-k + capacity
  *   moe_dispatch     expert-contiguous permutation of token rows   (local dispatch)
  *   moe_expert_ffn   grouped SwiGLU FFN = moe_expert_gate_up + moe_expert_down
  *   moe_combine      weighted sum of each token's expert rows     (combine)
@@ -87,7 +88,8 @@ typedef enum {
   MOE_OP_DISPATCH = 1,
   MOE_OP_FFN = 2, /* moe_expert_ffn; FP8 problems: also moe_expert_gate_up(_gather) */
   MOE_OP_COMBINE = 3,
-  MOE_OP_LAYER = 4
+  MOE_OP_LAYER = 4,
+  MOE_OP_ROUTER = 5 /* moe_router: split-K partial logits (+ capacity scratch) */
 } moe_op;
 
 typedef enum { MOE_W_GATE_UP = 0, MOE_W_DOWN = 1 } moe_weight_set;
@@ -148,6 +150,43 @@ int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
  * --------------------------------------------------------------------------------- */
 int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, float* topk_w,
               uint8_t* keep, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_route_grouped -- [LightLLM] call-order paragraph: `experts()` does grouped top-k
+ * inside the layer.  The pages do not give the group rule; this is its plain reading:
+ * the E experts form n_group groups of E / n_group consecutive ids, a group's score is
+ * its largest logit, the topk_group best groups are taken (ties to the lower group
+ * index), and the top-k of the experts in the taken groups are selected (order, ties,
+ * weights, renormalisation and capacity exactly as moe_route).  n_group = 1 (or
+ * topk_group = n_group) is moe_route.
+ * MOE_ERR_INVALID_ARG unless 1 <= topk_group <= n_group <= 64, n_group divides E and
+ * k <= topk_group * E / n_group.  Workspace: moe_workspace_bytes(p, MOE_OP_ROUTE).
+ * --------------------------------------------------------------------------------- */
+int moe_route_grouped(const moe_problem* p, const float* logits, int32_t n_group,
+                      int32_t topk_group, int32_t* topk_ids, float* topk_w, uint8_t* keep,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_router -- the routing front-end from the hidden states ([LightLLM] call-order
+ * paragraph: the layer's `experts()` computes its routing itself): a linear gate without
+ * bias, logits[t, e] = sum_h x[t, h] * w_router[e, h] (bf16 operands, fp32 accumulation
+ * on the matrix cores), then the selection of moe_route_grouped and the capacity, in one
+ * launch (plus the capacity kernels when capacity > 0).
+ *   x        [T, H] bf16      hidden states (16-byte aligned)
+ *   w_router [E, H] bf16      gate weights, one row per expert (the layout of a
+ *                             bias-free linear layer's weight; 16-byte aligned)
+ *   logits   [T, E] f32 or NULL: receives the logits (not needed by the selection)
+ *   topk_ids, topk_w, keep    as moe_route
+ * The selection is taken on the fp32 logits this call computes: the GEMM is split along
+ * H into S equal slices (S chosen from T and H so that the grid fills the chip) whose
+ * partial sums go to the workspace and are added in slice order by the selection kernel.
+ * Workspace: moe_workspace_bytes(p, MOE_OP_ROUTER).
+ * MOE_ERR_UNSUPPORTED unless act_dtype is bf16, E <= 256 and E is a multiple of 16;
+ * MOE_ERR_INVALID_ARG for the group arguments as in moe_route_grouped.
+ * --------------------------------------------------------------------------------- */
+int moe_router(const moe_problem* p, const void* x, const void* w_router, int32_t n_group,
+               int32_t topk_group, float* logits, int32_t* topk_ids, float* topk_w,
+               uint8_t* keep, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
  * moe_dispatch -- [LightLLM] expert prefix-sum layout (`use_psum_layout`); [WideEP]:

@@ -143,6 +143,14 @@ def make_weights(wl: Workload, device="cpu", experts: Optional[range] = None):
     return wg, wu, wd
 
 
+def make_router_weights(wl: Workload, device="cpu") -> torch.Tensor:
+    """Gate weights W_r [E, H] ~ N(0, 1/sqrt(H)) in bf16, so that x W_r^T has logits of
+    order 1 like the logits recipes."""
+    g = _gen(device, wl.seed, 4)
+    return (torch.randn(wl.E, wl.H, generator=g, device=device, dtype=torch.float32)
+            / math.sqrt(wl.H)).to(torch.bfloat16)
+
+
 def make_inputs(wl: Workload, device="cpu"):
     """All inputs of one layer call: dict(x, logits, w_gate, w_up, w_down)."""
     wg, wu, wd = make_weights(wl, device)

@@ -138,3 +138,33 @@ def test_quantize_fp8_rejects_bad_arguments(moe):
     assert q(ctypes.c_void_p(8), ctypes.c_int64(4), ctypes.c_int32(64), fake, fake,
              None) == moe.MOE_ERR_INVALID_ARG
     assert q(None, ctypes.c_int64(0), ctypes.c_int32(64), None, None, None) == moe.MOE_OK
+
+
+def test_router_workspace_holds_the_partial_logits(moe):
+    # split-K partial planes [S][T][E] f32 with S >= 1, plus the capacity scratch with a cap
+    p = moe.Problem(T=16384, H=7168, E=256, k=8, I=2048)
+    base = p.workspace_bytes(moe.OP_ROUTER)
+    assert base >= 16384 * 256 * 4 and base % (16384 * 256 * 4) == 0
+    capped = moe.Problem(T=16384, H=7168, E=256, k=8, I=2048, capacity=4096)
+    assert capped.workspace_bytes(moe.OP_ROUTER) > base
+    assert moe.Problem(T=8, H=64, E=320, k=2, I=64).workspace_bytes(moe.OP_ROUTER) == 0
+    # grouped routing from logits needs no scratch without a cap
+    assert p.workspace_bytes(moe.OP_ROUTE) == 0
+
+
+def test_router_and_grouped_route_reject_bad_arguments(moe):
+    fake = ctypes.c_void_p(256)
+    p = moe.Problem(T=64, H=128, E=64, k=4, I=128).c()
+    P = ctypes.byref(p)
+    gr = moe.lib.moe_route_grouped
+    assert gr(P, fake, 3, 1, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 64 % 3
+    assert gr(P, fake, 8, 9, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 9 > 8
+    assert gr(P, fake, 64, 2, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # k > 2
+    assert gr(P, fake, 128, 1, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    r = moe.lib.moe_router
+    assert r(P, fake, fake, 1, 1, None, fake, fake, fake, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert r(P, ctypes.c_void_p(8), fake, 1, 1, None, fake, fake, fake, None, 0,
+             None) == moe.MOE_ERR_INVALID_ARG
+    f32 = moe.Problem(T=64, H=128, E=64, k=4, I=128, dtype="f32").c()
+    assert r(ctypes.byref(f32), fake, fake, 1, 1, None, fake, fake, fake, None, 0,
+             None) == moe.MOE_ERR_UNSUPPORTED
