@@ -204,8 +204,11 @@ def ffn_rows(xrows: np.ndarray, row_expert: np.ndarray, w_gate: np.ndarray, w_up
     return (yp, a) if want_a else yp
 
 
-def combine(tokens: np.ndarray, topk_w: np.ndarray, slot_to_row: np.ndarray, yp: np.ndarray) -> np.ndarray:
-    """y[i] = sum over kept slots j of token tokens[i]: w[t,j] * yp[slot_to_row[t,j]], fp64."""
+def combine(tokens: np.ndarray, topk_w: np.ndarray, slot_to_row: np.ndarray, yp: np.ndarray,
+            shared: Optional[np.ndarray] = None) -> np.ndarray:
+    """y[i] = sum over kept slots j of token tokens[i]: w[t,j] * yp[slot_to_row[t,j]], fp64;
+    plus shared[i] (the shared expert's output for that token, [LightLLM] PR body: the
+    combine adds the shared expert's output) if given."""
     tokens = np.ascontiguousarray(tokens, dtype=np.int32)
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
     s2r = np.ascontiguousarray(slot_to_row, dtype=np.int32)
@@ -214,7 +217,17 @@ def combine(tokens: np.ndarray, topk_w: np.ndarray, slot_to_row: np.ndarray, yp:
     H = yp.shape[1]
     y = np.zeros((tokens.size, H), np.float64)
     _load().orc_combine(tokens.size, _p(tokens), H, k, _p(topk_w), _p(s2r), _p(yp), _p(y))
+    if shared is not None:
+        y = y + np.asarray(shared, dtype=np.float64)
     return y
+
+
+def shared_expert(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray,
+                  nthreads: int = 0) -> np.ndarray:
+    """The shared expert: the SwiGLU MLP of one expert ([1, H, Is] / [1, Is, H] weights)
+    applied to every row of x, fp64 (ffn_rows with every row on expert 0)."""
+    rows = np.zeros(x.shape[0], np.int32)
+    return ffn_rows(x, rows, w_gate, w_up, w_down, nthreads=nthreads)
 
 
 def layer(x: np.ndarray, logits: np.ndarray, w_gate, w_up, w_down, k: int, capacity_: int = 0,

@@ -123,3 +123,28 @@ def test_router_logits_pins():
     got_b = oracle.router_logits(bits(xb), bits(wb))
     ref_b = xb.double().numpy() @ wb.double().numpy().T
     assert np.allclose(got_b, ref_b, rtol=1e-12, atol=1e-12)
+
+
+def test_combine_with_shared_expert():
+    """y = routed combine + shared expert output: zero shared output leaves the combine
+    unchanged; a token with every slot dropped gets exactly the shared output; the shared
+    expert is the one-expert dense SwiGLU MLP (numpy fp64)."""
+    rng = np.random.default_rng(21)
+    T, H, k, Is = 6, 16, 2, 24
+    yp = rng.standard_normal((T * k, H))
+    w = rng.random((T, k)).astype(np.float32)
+    s2r = np.arange(T * k, dtype=np.int32).reshape(T, k)
+    s2r[2] = -1                                            # token 2: every slot dropped
+    toks = np.arange(T, dtype=np.int32)
+    base = oracle.combine(toks, w, s2r, yp)
+    assert np.array_equal(oracle.combine(toks, w, s2r, yp, np.zeros((T, H))), base)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    wg, wu = (rng.standard_normal((1, H, Is)).astype(np.float32) for _ in range(2))
+    wd = rng.standard_normal((1, Is, H)).astype(np.float32)
+    sh = oracle.shared_expert(x, wg, wu, wd)
+    g, u = x.astype(np.float64) @ wg[0].astype(np.float64), x.astype(np.float64) @ wu[0].astype(np.float64)
+    ref = (g / (1.0 + np.exp(-g)) * u) @ wd[0].astype(np.float64)
+    assert np.allclose(sh, ref, rtol=1e-12, atol=1e-12)
+    y = oracle.combine(toks, w, s2r, yp, sh)
+    assert np.array_equal(y[2], sh[2])
+    assert np.allclose(y - sh, base, rtol=0, atol=1e-12)
