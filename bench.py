@@ -46,6 +46,11 @@ def parse():
                     help="route from the hidden states: router GEMM x W_r^T + selection "
                          "(moe_router; DeepSeek-V3-style 8/4 expert groups when E = 256) instead "
                          "of moe_route on given logits")
+    ap.add_argument("--chunk-tokens", type=int, default=0,
+                    help="also time moe_layer and moe_layer_chunked with chunks of this many "
+                         "tokens (layouts on an auxiliary stream); reported under 'layer_calls'")
+    ap.add_argument("--shared-I", type=int, default=0,
+                    help="with --chunk-tokens: a shared expert of this intermediate width")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -169,6 +174,52 @@ def cpu_baseline(wl, inp, target_s, wr=None, groups=(1, 1)):
                        f"over {n} random tokens ({t_ffn:.2f} s), scaled to {wl.T} tokens")
 
 
+def time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev):
+    """ms per call of moe_layer and of moe_layer_chunked (with an auxiliary stream, and with
+    a shared expert if asked), every buffer allocated before timing."""
+    import torch
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return round((time.perf_counter() - t0) / args.steps * 1e3, 4)
+
+    y = torch.empty(wl.T, wl.H, dtype=p.torch_dtype, device=dev)
+    ws_l = moe.workspace(p, moe.OP_LAYER, dev)
+    res = {"layer_ms": timed(lambda: moe.layer(p, inp["x"], inp["logits"], pgu, pd, out=y,
+                                                ws=ws_l))}
+    shared = None
+    if args.shared_I > 0:
+        g = torch.Generator(device=dev)
+        g.manual_seed(12345)
+        I = args.shared_I
+        sw = [(torch.randn(1, wl.H, I, generator=g, device=dev) / wl.H ** 0.5).to(torch.bfloat16),
+              (torch.randn(1, wl.H, I, generator=g, device=dev) / wl.H ** 0.5).to(torch.bfloat16),
+              (torch.randn(1, I, wl.H, generator=g, device=dev) / I ** 0.5).to(torch.bfloat16)]
+        spgu, spd = moe.pack_weights(moe.shared_problem(p, I), *sw)
+        shared = (I, spgu, spd)
+    aux = torch.cuda.Stream()
+    c = p.c()
+    import ctypes
+    need = int(moe.lib.moe_layer_chunked_workspace_bytes(ctypes.byref(c), args.chunk_tokens,
+                                                         args.shared_I))
+    ws_c = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    res["chunk_tokens"] = args.chunk_tokens
+    res["shared_I"] = args.shared_I
+    res["chunked_ms"] = timed(lambda: moe.layer_chunked(p, inp["x"], inp["logits"], pgu, pd,
+                                                        args.chunk_tokens, shared=shared,
+                                                        aux_stream=aux, out=y, ws=ws_c))
+    res["chunked_one_stream_ms"] = timed(lambda: moe.layer_chunked(
+        p, inp["x"], inp["logits"], pgu, pd, args.chunk_tokens, shared=shared, out=y, ws=ws_c))
+    res["workspace_bytes"] = {"layer": int(ws_l.numel()), "chunked": need}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -264,6 +315,9 @@ def main():
     per_stage = {s: dict(us=round(stage_ms[s] * 1e3, 2),
                          **{k: v for k, v in roofline_of(s, alg, stage_ms[s] / 1e3, wl.dtype).items()
                             if k in ("bound", "achieved", "unit", "frac")}) for s in stages}
+    layer_calls = None
+    if args.chunk_tokens > 0:
+        layer_calls = time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev)
     out = {
         "metric": METRIC, "value": round(wl.T / sec, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
@@ -273,6 +327,8 @@ def main():
                    "capacity": wl.capacity, "N_kept": N, "experts_hit": E_hit},
         "roofline": roof, "stages": per_stage,
     }
+    if layer_calls is not None:
+        out["layer_calls"] = layer_calls
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, wr, groups)
     print(json.dumps(out), flush=True)

@@ -36,13 +36,19 @@ EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_pa
            "moe_pack_weights", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_gate_up",
            "moe_expert_gate_up_gather",
            "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
-           "moe_route_grouped", "moe_router")
+           "moe_route_grouped", "moe_router", "moe_layer_chunked_workspace_bytes",
+           "moe_layer_chunked")
 
 
 class MoeError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: {status_str(status)} ({status})")
+
+
+class MoeSharedExpert(ctypes.Structure):
+    _fields_ = [("I", ctypes.c_int32), ("packed_gate_up", ctypes.c_void_p),
+                ("packed_down", ctypes.c_void_p)]
 
 
 class MoeProblem(ctypes.Structure):
@@ -77,6 +83,9 @@ def _load() -> ctypes.CDLL:
                                              sz, P]),
         "moe_router": (ctypes.c_int, [PP, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
                                       sz, P]),
+        "moe_layer_chunked_workspace_bytes": (sz, [PP, ctypes.c_int32, ctypes.c_int32]),
+        "moe_layer_chunked": (ctypes.c_int, [PP, P, P, P, P, ctypes.POINTER(MoeSharedExpert),
+                                             ctypes.c_int32, P, P, sz, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -389,6 +398,35 @@ def quantize_fp8(x, codes=None, scales=None):
     _call("moe_quantize_fp8", _ptr(x), ctypes.c_int64(rows), ctypes.c_int32(cols), _ptr(codes),
           _ptr(scales), _stream())
     return codes, scales
+
+
+def shared_problem(p: Problem, I: int) -> Problem:
+    """The one-expert problem whose packed weights a shared expert of width I uses."""
+    return dataclasses.replace(p, E=1, k=1, I=I, capacity=0)
+
+
+def layer_chunked(p: Problem, x, logits, packed_gate_up, packed_down, chunk_tokens: int,
+                  shared=None, aux_stream=None, out=None, ws=None):
+    """The layer over chunks of tokens (see moe_layer_chunked).  shared: None or
+    (I, packed_gate_up, packed_down) of the shared expert; aux_stream: a torch stream for
+    the layouts (and the shared expert), or None."""
+    dt = p.torch_dtype
+    _need(x, "x", (p.T, p.H), dt)
+    _need(logits, "logits", (p.T, p.E), torch.float32)
+    y = _empty((p.T, p.H), dt, x.device) if out is None else out
+    sI = 0 if shared is None else int(shared[0])
+    c = p.c()
+    need = int(lib.moe_layer_chunked_workspace_bytes(ctypes.byref(c), int(chunk_tokens), sI))
+    if ws is None:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    sh = None
+    if shared is not None:
+        sh = MoeSharedExpert(sI, shared[1].data_ptr(), shared[2].data_ptr())
+    aux = None if aux_stream is None else ctypes.c_void_p(aux_stream.cuda_stream)
+    _call("moe_layer_chunked", ctypes.byref(c), _ptr(x), _ptr(logits), _ptr(packed_gate_up),
+          _ptr(packed_down), None if sh is None else ctypes.byref(sh), int(chunk_tokens), _ptr(y),
+          _ptr(ws), ws.numel(), _stream(), aux)
+    return y
 
 
 def routing_buffers(p: Problem, device="cuda"):

@@ -1,7 +1,9 @@
 // Combine (LightLLM PR #1687 walkthrough, "Synchronous prefill and decode execution":
 // expert outputs are reduced into dense token output):
 //   y[t] = sum over slots j in order, skipping dropped ones, of w[t,j] * yp[slot_to_row[t,j]]
-// fp32 accumulation in slot order, one token per block: deterministic, no atomics.
+// fp32 accumulation in slot order, one token per block: deterministic, no atomics.  With a
+// shared expert (PR body: the combine adds the shared expert's output), its row for the
+// token is added last, before the one rounding.
 #include "bf16.h"
 #include "moe_internal.h"
 
@@ -12,6 +14,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ s2r,
                                                            int k, int nvec,
+                                                           const uint4* __restrict__ shared,
                                                            uint4* __restrict__ y) {
   __shared__ int rows[32];
   __shared__ float wt[32];
@@ -32,6 +35,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
     }
+    if (shared) {
+      float f[8];
+      unpack8(shared[(size_t)t * nvec + v], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + f[i];
+    }
     y[(size_t)t * nvec + v] = pack8(acc);
   }
 }
@@ -40,6 +49,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
                                                           const float* __restrict__ w,
                                                           const int32_t* __restrict__ s2r,
                                                           int k, int nvec,
+                                                          const float4* __restrict__ shared,
                                                           float4* __restrict__ y) {
   __shared__ int rows[32];
   __shared__ float wt[32];
@@ -61,20 +71,38 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
       acc.z = __builtin_fmaf(wj, f.z, acc.z);
       acc.w = __builtin_fmaf(wj, f.w, acc.w);
     }
+    if (shared) {
+      const float4 f = shared[(size_t)t * nvec + v];
+      acc.x = acc.x + f.x;
+      acc.y = acc.y + f.y;
+      acc.z = acc.z + f.z;
+      acc.w = acc.w + f.w;
+    }
     y[(size_t)t * nvec + v] = acc;
   }
+}
+
+// offsets of a one-expert layout of n rows: {0, n}
+__global__ void one_expert_offsets_kernel(int32_t* off, int n) {
+  if (threadIdx.x < 2) off[threadIdx.x] = threadIdx.x ? n : 0;
 }
 
 }  // namespace
 
 hipError_t launch_combine(const moe_problem& p, const void* yp, const float* w,
-                          const int32_t* slot_to_row, void* y, hipStream_t s) {
-  if (p.act_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
-                       slot_to_row, p.k, p.H / 8, (uint4*)y);
-  else
+                          const int32_t* slot_to_row, const void* shared, void* y,
+                          hipStream_t s) {
+  if (p.act_dtype == MOE_F32)
     hipLaunchKernelGGL(combine_f32_kernel, dim3(p.T), dim3(256), 0, s, (const float4*)yp, w,
-                       slot_to_row, p.k, p.H / 4, (float4*)y);
+                       slot_to_row, p.k, p.H / 4, (const float4*)shared, (float4*)y);
+  else
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
+                       slot_to_row, p.k, p.H / 8, (const uint4*)shared, (uint4*)y);
+  return hipGetLastError();
+}
+
+hipError_t launch_one_expert_offsets(int32_t* off, int n, hipStream_t s) {
+  hipLaunchKernelGGL(one_expert_offsets_kernel, dim3(1), dim3(64), 0, s, off, n);
   return hipGetLastError();
 }
 

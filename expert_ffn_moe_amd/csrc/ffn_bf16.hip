@@ -437,8 +437,9 @@ int persistent_grid() { return std::max(kXcds, cu_count() / kXcds * kXcds); }
 namespace {
 template <bool GATHER>
 void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
-                  const int32_t* offsets, const void* packed_gu, void* a, hipStream_t s) {
-  if (ffn_use_decode(p)) {
+                  const int32_t* offsets, const void* packed_gu, void* a, bool decode,
+                  hipStream_t s) {
+  if (decode) {
     const int nf32 = p.I / 32;
     hipLaunchKernelGGL((decode_kernel<true, GATHER>), dim3(div_up(nf32, 4), p.E), dim3(256), 0,
                        s, (const uint16_t*)xs, row_token, offsets, (const uint16_t*)packed_gu,
@@ -453,17 +454,17 @@ void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token
 
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
                                const int32_t* offsets, const void* packed_gu, void* a,
-                               hipStream_t s) {
+                               bool decode, hipStream_t s) {
   if (row_token)
-    gate_up_bf16<true>(p, xs, row_token, offsets, packed_gu, a, s);
+    gate_up_bf16<true>(p, xs, row_token, offsets, packed_gu, a, decode, s);
   else
-    gate_up_bf16<false>(p, xs, nullptr, offsets, packed_gu, a, s);
+    gate_up_bf16<false>(p, xs, nullptr, offsets, packed_gu, a, decode, s);
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, hipStream_t s) {
-  if (ffn_use_decode(p)) {
+                            const void* packed_d, void* yp, bool decode, hipStream_t s) {
+  if (decode) {
     const int nf32 = p.H / 32;
     hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
                        0, s, (const uint16_t*)a, nullptr, offsets, (const uint16_t*)packed_d,

@@ -3,6 +3,8 @@
 // to fall back to.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -58,6 +60,74 @@ FfnScratch carve_ffn(Carve& c, const moe_problem& p) {
     f.a = c.take<char>(tk * p.I * elem_bytes(p.act_dtype));
   }
   return f;
+}
+
+// ---- chunked layer: the whole layer's routing, then per chunk of tokens a layout (two
+// sets, so that the next chunk's can be built on the aux stream while the current one is
+// in use), the routed FFN and the combine; optional shared-expert rows per set.
+moe_problem shared_problem(const moe_problem& p, int rows, int shared_I) {
+  moe_problem ps = p;
+  ps.T = rows;
+  ps.E = 1;
+  ps.k = 1;
+  ps.I = shared_I;
+  ps.capacity = 0;
+  return ps;
+}
+
+int chunked_check(const moe_problem* p, int chunk_tokens, int shared_I) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (chunk_tokens < 1 || shared_I < 0) return MOE_ERR_INVALID_ARG;
+  if (shared_I > 0) {
+    moe_problem ps = shared_problem(*p, std::min(chunk_tokens, p->T), shared_I);
+    if ((st = moe_problem_check(&ps)) != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+struct ChunkSet {
+  int32_t *counts, *offsets, *row_token, *slot_to_row, *s_off;
+  RankScratch rank;
+  FfnScratch s_ffn;  // shared expert's intermediate (and quantised rows)
+  void* ys;          // shared expert's output rows
+};
+struct ChunkScratch {
+  int32_t* ids;
+  float* w;
+  uint8_t* keep;
+  RankScratch rank;  // capacity over all T
+  ChunkSet set[2];
+  FfnScratch ffn;    // routed intermediate of one chunk
+  void* yp;
+};
+ChunkScratch carve_chunked(Carve& c, const moe_problem& p, int chunk_tokens, int shared_I) {
+  const int tc = std::min(chunk_tokens, p.T);
+  const size_t tk = (size_t)p.T * p.k, ck = (size_t)tc * p.k;
+  const size_t eb = elem_bytes(p.act_dtype);
+  moe_problem pc = p;
+  pc.T = tc;
+  ChunkScratch S{};
+  S.ids = c.take<int32_t>(tk);
+  S.w = c.take<float>(tk);
+  S.keep = c.take<uint8_t>(tk);
+  S.rank = p.capacity > 0 ? carve_rank(c, p, true) : RankScratch{};
+  for (int i = 0; i < 2; ++i) {
+    ChunkSet& L = S.set[i];
+    L.counts = c.take<int32_t>(p.E);
+    L.offsets = c.take<int32_t>((size_t)p.E + 1);
+    L.row_token = c.take<int32_t>(ck);
+    L.slot_to_row = c.take<int32_t>(ck);
+    L.rank = carve_rank(c, pc, false);
+    if (shared_I > 0) {
+      L.s_off = c.take<int32_t>(2);
+      L.s_ffn = carve_ffn(c, shared_problem(p, tc, shared_I));
+      L.ys = c.take<char>((size_t)tc * p.H * eb);
+    }
+  }
+  S.ffn = carve_ffn(c, pc);
+  S.yp = c.take<char>(ck * p.H * eb);
+  return S;
 }
 
 struct LayerScratch {
@@ -183,9 +253,10 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
 
 // Gate/up over the layout: rows xs[r], or token rows xs[row_token[r]] if row_token != NULL.
 // FP8: the input rows (T token rows, or T*k rows of xp) are quantised into f.xq first.
+// decode: which bf16 kernel family (ffn_use_decode of the problem the rows belong to).
 hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_token,
                        const int32_t* offsets, const void* pgu, void* a, const FfnScratch& f,
-                       hipStream_t s) {
+                       bool decode, hipStream_t s) {
   if (is_fp8(p)) {
     const size_t tk = (size_t)p.T * p.k;
     const size_t rows = row_token ? (size_t)p.T : tk;
@@ -203,11 +274,11 @@ hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_
     return launch_gate_up_f32(p, (const float*)xs, row_token, offsets, (const float*)pgu,
                               (const float*)pgu + n, (float*)a, s);
   }
-  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, s);
+  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, decode, s);
 }
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
-                    const void* pd, void* yp, hipStream_t s) {
+                    const void* pd, void* yp, bool decode, hipStream_t s) {
   if (is_fp8(p)) {
     const size_t tk = (size_t)p.T * p.k;
     return launch_down_fp8(p, static_cast<const uint8_t*>(a),
@@ -215,7 +286,7 @@ hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
   }
   if (p.act_dtype == MOE_F32)
     return launch_down_f32(p, (const float*)a, offsets, (const float*)pd, (float*)yp, s);
-  return launch_down_bf16(p, a, offsets, pd, yp, s);
+  return launch_down_bf16(p, a, offsets, pd, yp, decode, s);
 }
 
 }  // namespace
@@ -370,7 +441,8 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
     if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   }
   return status_of(
-      run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, f, as_stream(stream)));
+      run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, a, f,
+                  ffn_use_decode(*p), as_stream(stream)));
 }
 
 int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t* row_token,
@@ -388,7 +460,8 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
     if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   }
   return status_of(
-      run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, f, as_stream(stream)));
+      run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, f,
+                  ffn_use_decode(*p), as_stream(stream)));
 }
 
 int moe_quantize_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
@@ -408,7 +481,8 @@ int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
   if (!aligned16(a) || !aligned16(packed_down) || !aligned16(yp)) return MOE_ERR_INVALID_ARG;
   (void)ws;
   (void)ws_bytes;
-  return status_of(run_down(*p, a, offsets, packed_down, yp, as_stream(stream)));
+  return status_of(
+      run_down(*p, a, offsets, packed_down, yp, ffn_use_decode(*p), as_stream(stream)));
 }
 
 int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
@@ -425,8 +499,9 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   FfnScratch f = carve_ffn(c, *p);
   if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   hipStream_t s = as_stream(stream);
-  hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, f, s);
-  if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, s);
+  const bool dec = ffn_use_decode(*p);
+  hipError_t err = run_gate_up(*p, xp, nullptr, offsets, packed_gate_up, f.a, f, dec, s);
+  if (err == hipSuccess) err = run_down(*p, f.a, offsets, packed_down, yp, dec, s);
   return status_of(err);
 }
 
@@ -436,7 +511,7 @@ int moe_combine(const moe_problem* p, const void* yp, const float* topk_w,
   if (st != MOE_OK) return st;
   if (!yp || !topk_w || !slot_to_row || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(yp) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
-  return status_of(launch_combine(*p, yp, topk_w, slot_to_row, y, as_stream(stream)));
+  return status_of(launch_combine(*p, yp, topk_w, slot_to_row, nullptr, y, as_stream(stream)));
 }
 
 int moe_layer(const moe_problem* p, const void* x, const float* logits,
@@ -467,9 +542,98 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
                        row_token, slot_to_row, nullptr, L.rank, s);
   if (err == hipSuccess)
-    err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, L.ffn, s);
-  if (err == hipSuccess) err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, s);
-  if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, y, s);
+    err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, L.ffn,
+                      ffn_use_decode(*p), s);
+  if (err == hipSuccess)
+    err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, ffn_use_decode(*p), s);
+  if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, nullptr, y, s);
+  return status_of(err);
+}
+
+size_t moe_layer_chunked_workspace_bytes(const moe_problem* p, int32_t chunk_tokens,
+                                         int32_t shared_I) {
+  if (chunked_check(p, chunk_tokens, shared_I) != MOE_OK) return 0;
+  Carve c(nullptr);
+  carve_chunked(c, *p, chunk_tokens, shared_I);
+  return c.used;
+}
+
+int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
+                      const void* packed_gate_up, const void* packed_down,
+                      const moe_shared_expert* shared, int32_t chunk_tokens, void* y, void* ws,
+                      size_t ws_bytes, void* stream, void* aux_stream) {
+  const int shared_I = shared ? shared->I : 0;
+  int st = chunked_check(p, chunk_tokens, shared_I);
+  if (st != MOE_OK) return st;
+  if (!x || !logits || !packed_gate_up || !packed_down || !y) return MOE_ERR_INVALID_ARG;
+  if (shared && (!shared->packed_gate_up || !shared->packed_down ||
+                 !aligned16(shared->packed_gate_up) || !aligned16(shared->packed_down)))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(packed_gate_up) || !aligned16(packed_down))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need = moe_layer_chunked_workspace_bytes(p, chunk_tokens, shared_I);
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  if (((uintptr_t)ws & 255) != 0) return MOE_ERR_INVALID_ARG;
+  Carve c(ws);
+  ChunkScratch S = carve_chunked(c, *p, chunk_tokens, shared_I);
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;
+
+  hipStream_t s = as_stream(stream);
+  hipStream_t aux = aux_stream ? as_stream(aux_stream) : s;
+  const bool two = aux != s;
+  hipEvent_t ev[5] = {};  // route done, layout set 0/1 ready, layout set 0/1 free again
+  hipError_t err = hipSuccess;
+  if (two)
+    for (int i = 0; i < 5 && err == hipSuccess; ++i)
+      err = hipEventCreateWithFlags(&ev[i], hipEventDisableTiming);
+  const size_t eb = elem_bytes(p->act_dtype);
+  const char* xb = static_cast<const char*>(x);
+  char* yb = static_cast<char*>(y);
+
+  // routing and the capacity over all T tokens: the result does not depend on the chunking
+  if (err == hipSuccess) err = run_route(*p, logits, 1, 1, S.ids, S.w, S.keep, S.rank, s);
+  if (err == hipSuccess && two) err = hipEventRecord(ev[0], s);
+  if (err == hipSuccess && two) err = hipStreamWaitEvent(aux, ev[0], 0);
+  const int nchunks = div_up(p->T, chunk_tokens);
+  // kernel families of the whole layer, so that no row's result depends on the chunking
+  const bool dec = ffn_use_decode(*p);
+  const bool dec_shared = ffn_use_decode(shared_problem(*p, p->T, std::max(shared_I, 1)));
+  for (int ci = 0; ci < nchunks && err == hipSuccess; ++ci) {
+    const int t0 = ci * chunk_tokens;
+    const int n = std::min(chunk_tokens, p->T - t0);
+    const ChunkSet& L = S.set[ci & 1];
+    moe_problem pc = *p;
+    pc.T = n;
+    // aux: the chunk's layout (and its shared-expert rows), once set ci & 1 is free again
+    if (two && ci >= 2) err = hipStreamWaitEvent(aux, ev[3 + (ci & 1)], 0);
+    if (err == hipSuccess)
+      err = run_dispatch(pc, xb + (size_t)t0 * p->H * eb, S.ids + (size_t)t0 * p->k,
+                         p->capacity > 0 ? S.keep + (size_t)t0 * p->k : nullptr, L.counts,
+                         L.offsets, L.row_token, L.slot_to_row, nullptr, L.rank, aux);
+    if (err == hipSuccess && shared_I > 0) {
+      moe_problem ps = shared_problem(*p, n, shared_I);
+      err = launch_one_expert_offsets(L.s_off, n, aux);
+      if (err == hipSuccess)
+        err = run_gate_up(ps, xb + (size_t)t0 * p->H * eb, nullptr, L.s_off,
+                          shared->packed_gate_up, L.s_ffn.a, L.s_ffn, dec_shared, aux);
+      if (err == hipSuccess)
+        err = run_down(ps, L.s_ffn.a, L.s_off, shared->packed_down, L.ys, dec_shared, aux);
+    }
+    if (err == hipSuccess && two) err = hipEventRecord(ev[1 + (ci & 1)], aux);
+    // main: the routed experts of the chunk and its combine
+    if (err == hipSuccess && two) err = hipStreamWaitEvent(s, ev[1 + (ci & 1)], 0);
+    if (err == hipSuccess)
+      err = run_gate_up(pc, xb + (size_t)t0 * p->H * eb, L.row_token, L.offsets,
+                        packed_gate_up, S.ffn.a, S.ffn, dec, s);
+    if (err == hipSuccess) err = run_down(pc, S.ffn.a, L.offsets, packed_down, S.yp, dec, s);
+    if (err == hipSuccess)
+      err = launch_combine(pc, S.yp, S.w + (size_t)t0 * p->k, L.slot_to_row,
+                           shared_I > 0 ? L.ys : nullptr, yb + (size_t)t0 * p->H * eb, s);
+    if (err == hipSuccess && two) err = hipEventRecord(ev[3 + (ci & 1)], s);
+  }
+  // events are released once the work recorded on them has completed
+  for (int i = 0; i < 5; ++i)
+    if (ev[i]) (void)hipEventDestroy(ev[i]);
   return status_of(err);
 }
 

@@ -83,22 +83,28 @@ hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slo
                          void* xp, hipStream_t s);
 
 // ---- combine.hip
+// shared: NULL, or the shared expert's output rows [T, H] (act dtype), added last.
 hipError_t launch_combine(const moe_problem& p, const void* yp, const float* w,
-                          const int32_t* slot_to_row, void* y, hipStream_t s);
+                          const int32_t* slot_to_row, const void* shared, void* y,
+                          hipStream_t s);
+// off[0] = 0, off[1] = n (the layout of a one-expert problem over n rows).
+hipError_t launch_one_expert_offsets(int32_t* off, int n, hipStream_t s);
 
 // ---- pack.hip
 hipError_t launch_pack(const moe_problem& p, const void* wg, const void* wu, const void* wd,
                        void* packed_gu, void* packed_d, hipStream_t s);
 
 // ---- ffn_bf16.hip / ffn_f32.hip
+// The decode-shaped kernels (few rows per expert) or the prefill ones: decided from the
+// whole problem (a chunked layer decides once, so every chunk uses the same kernels).
 bool ffn_use_decode(const moe_problem& p);
 // Gate/up over the layout's rows: row r reads xs[r] (xp), or xs[row_token[r]] (token rows
 // x) when row_token is not NULL.
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
                                const int32_t* offsets, const void* packed_gu, void* a,
-                               hipStream_t s);
+                               bool decode, hipStream_t s);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, hipStream_t s);
+                            const void* packed_d, void* yp, bool decode, hipStream_t s);
 hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32_t* row_token,
                               const int32_t* offsets, const float* wg, const float* wu, float* a,
                               hipStream_t s);

@@ -8,6 +8,8 @@
  *   moe_expert_ffn   grouped SwiGLU FFN = moe_expert_gate_up + moe_expert_down
  *   moe_combine      weighted sum of each token's expert rows     (combine)
  *   moe_layer        all of the above on one stream
+ *   moe_layer_chunked  the layer over chunks of tokens, layouts on a second stream,
+ *                    optional shared expert
  *
  * The pages describe the operations in prose; each declaration names the passage:
  *   [axolotl]  docs.axolotl.ai "integrations.expert_parallel.args", attribute table
@@ -284,6 +286,45 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
               int32_t* topk_ids, float* topk_w, uint8_t* keep, int32_t* counts,
               int32_t* offsets, int32_t* row_token, int32_t* slot_to_row, void* ws,
               size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------
+ * moe_layer_chunked -- moe_layer over chunks of tokens, with the next chunk's layout
+ * built on a second stream while the current chunk's experts run, and an optional shared
+ * expert ([LightLLM] PR body: the chunked expanded forward bounds each call's temporary
+ * rows (at most 32K there); the shared expert's output is added in the combine, its
+ * computation overlapped with the routed experts on the other stream).
+ *
+ * Routing and the capacity are computed once over all T tokens on `stream` (so the result
+ * does not depend on the chunking: y equals moe_layer's bit for bit without a shared
+ * expert).  Then for each chunk of up to chunk_tokens tokens: its expert-contiguous layout
+ * (and the shared expert's rows) on `aux_stream`, the routed gate/up, down and the
+ * combine (which adds the shared rows last, in fp32, before the one rounding) on
+ * `stream`.  Two layout sets alternate; events order the two streams, so work issued
+ * later on `stream` sees the whole result.  aux_stream NULL (or equal to stream): all on
+ * `stream`.  Events are created and released inside the call (no device memory).
+ *
+ *   shared       NULL, or the shared expert: its intermediate width I and its weights
+ *                packed by moe_pack_weights for the problem {T, H, E = 1, k = 1, I,
+ *                same dtypes}; y[t] = routed combine + SwiGLU_shared(x[t]).
+ *   chunk_tokens >= 1 (clamped to T); the workspace grows with it, not with T (except
+ *                for the [T, k] routing results).
+ * Workspace: moe_layer_chunked_workspace_bytes(p, chunk_tokens, shared ? shared->I : 0)
+ * (0 if the arguments are invalid).  Errors as moe_layer; MOE_ERR_INVALID_ARG for
+ * chunk_tokens < 1 or a NULL shared weight; the shared problem must pass
+ * moe_problem_check (e.g. I a multiple of 64 for bf16).
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  int32_t I;                  /* the shared expert's intermediate width */
+  const void* packed_gate_up; /* moe_pack_weights output for {T, H, 1, 1, I} */
+  const void* packed_down;
+} moe_shared_expert;
+
+size_t moe_layer_chunked_workspace_bytes(const moe_problem* p, int32_t chunk_tokens,
+                                         int32_t shared_I);
+int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
+                      const void* packed_gate_up, const void* packed_down,
+                      const moe_shared_expert* shared, int32_t chunk_tokens, void* y, void* ws,
+                      size_t ws_bytes, void* stream, void* aux_stream);
 
 #ifdef __cplusplus
 }
