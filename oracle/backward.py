@@ -42,13 +42,15 @@ def _sigmoid(z):
 
 def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int = 0,
                    renormalize: int = 1, w_router: Optional[np.ndarray] = None,
-                   experts: Optional[np.ndarray] = None):
+                   experts: Optional[np.ndarray] = None, tokens: Optional[np.ndarray] = None):
     """Gradients of the layer for upstream gradient dy [T, H].
 
     x [T, H], w_gate/w_up [E, H, I], w_down [E, I, H] (f32/f64, or bf16 as uint16);
     logits [T, E] f32 (the routing is recomputed from them exactly as in the forward).
     experts: if given, the weight gradients are computed for these experts only (the
-    others are returned as zeros); dx and dlogits still need every expert a token uses.
+    others are returned as zeros); tokens: if given, dx, dlogits and dtopk_w are computed
+    for these tokens only (rows of other tokens are evaluated only where a listed expert's
+    weight gradient needs them; the other tokens' entries are left at zero).
     Returns dict(dx [T,H], dw_gate, dw_up [E,H,I], dw_down [E,I,H], dlogits [T,E],
     dtopk_w [T,k], yp [N,H], and dw_router [E,H] if w_router is given), fp64."""
     X = _f64(np.asarray(x))
@@ -63,9 +65,8 @@ def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int =
     rt, off = lay["row_token"][:N], lay["offsets"]
     s2r = lay["slot_to_row"]
     wsel = np.asarray(experts) if experts is not None else np.arange(E)
-    need = np.zeros(E, bool)
-    need[np.unique(ids[keep.astype(bool)])] = True
-    need[wsel] = True
+    tsel = np.zeros(T, bool)
+    tsel[np.asarray(tokens) if tokens is not None else np.arange(T)] = True
 
     # row -> (token, slot)
     row_t = np.empty(N, np.int64)
@@ -82,32 +83,41 @@ def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int =
     dW = np.zeros((T, k))
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
-        if r1 == r0 or not need[e]:
+        if r1 == r0:
             continue
-        xe = X[rt[r0:r1]]
+        if e in wsel:
+            rows = np.arange(r0, r1)
+        else:
+            rows = np.arange(r0, r1)[tsel[rt[r0:r1]]]
+            if rows.size == 0:
+                continue
+        xe = X[rt[rows]]
         g = xe @ Wg[e]
         u = xe @ Wu[e]
         sg = _sigmoid(g)
         a = g * sg * u
         ype = a @ Wd[e]
-        yp[r0:r1] = ype
-        dyt = dY[row_t[r0:r1]]
-        dyp = row_w[r0:r1, None] * dyt
+        yp[rows] = ype
+        dyt = dY[row_t[rows]]
+        dyp = row_w[rows, None] * dyt
         dwr = np.sum(ype * dyt, axis=1)
-        for q, r in enumerate(range(r0, r1)):
+        for q, r in enumerate(rows):
             t = row_t[r]
             j = int(np.nonzero(s2r[t] == r)[0][0])
             dW[t, j] = dwr[q]
         da = dyp @ Wd[e].T
         du = da * g * sg
         dg = da * u * sg * (1.0 + g * (1.0 - sg))
-        np.add.at(dX, rt[r0:r1], dg @ Wg[e].T + du @ Wu[e].T)
+        tok = rt[rows]
+        mine = tsel[tok]
+        np.add.at(dX, tok[mine], (dg @ Wg[e].T + du @ Wu[e].T)[mine])
         if e in wsel:
             dWd[e] = a.T @ dyp
             dWg[e] = xe.T @ dg
             dWu[e] = xe.T @ du
 
     # router: d logits from d w (dropped slots carry no gradient: dW is 0 there)
+    dW[~tsel] = 0.0
     L = np.asarray(logits, np.float64)
     wf = w.astype(np.float64)
     dL = np.zeros((T, E))

@@ -131,3 +131,14 @@ def test_backward_expert_subset_and_zero_upstream():
     zero = ob.layer_backward(x, lg, wg, wu, wd, 2, np.zeros_like(dy))
     for n in ("dx", "dw_gate", "dw_up", "dw_down", "dlogits"):
         assert not np.any(zero[n])
+
+
+def test_backward_token_subset():
+    x, lg, wg, wu, wd, _, dy = make(12, 8, 4, 2, 6, seed=4)
+    full = ob.layer_backward(x, lg, wg, wu, wd, 2, dy)
+    toks = np.array([0, 5, 11])
+    sub = ob.layer_backward(x, lg, wg, wu, wd, 2, dy, experts=np.array([2]), tokens=toks)
+    for n in ("dx", "dlogits", "dtopk_w"):
+        assert np.allclose(sub[n][toks], full[n][toks], rtol=1e-13, atol=1e-13), n
+    for n in ("dw_gate", "dw_up", "dw_down"):
+        assert np.allclose(sub[n][2], full[n][2], rtol=1e-13, atol=1e-13), n
