@@ -51,6 +51,9 @@ def parse():
                          "tokens (layouts on an auxiliary stream); reported under 'layer_calls'")
     ap.add_argument("--shared-I", type=int, default=0,
                     help="with --chunk-tokens: a shared expert of this intermediate width")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_layer_backward (saved routing and expert outputs of the "
+                         "timed forward, bf16 upstream gradient); reported under 'backward'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -220,6 +223,39 @@ def time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev):
     return res
 
 
+def time_backward(args, moe, p, wl, inp, pgu, pd, routing, disp, yp, dev):
+    """ms per moe_layer_backward call on the last forward's routing and expert outputs, and
+    the matrix-core rate over its GEMM flops (data gradients: da 2NHI, g|u recompute 4NHI,
+    dxp 4NHI; weight gradients 2NHI + 4NHI)."""
+    import torch
+
+    if wl.dtype != "bf16":
+        return {"skipped": "the backward pass takes bf16 problems"}
+    pbgu, pbd = moe.pack_weights_backward(p, inp["w_gate"], inp["w_up"], inp["w_down"])
+    g = torch.Generator(device=dev)
+    g.manual_seed(99)
+    dy = torch.randn(wl.T, wl.H, generator=g, device=dev).to(torch.bfloat16)
+    saved = dict(topk_ids=routing[0], topk_w=routing[1], offsets=disp["offsets"],
+                 row_token=disp["row_token"], slot_to_row=disp["slot_to_row"])
+    ws = moe.workspace(p, moe.OP_BACKWARD, dev)
+    fn = lambda: moe.layer_backward(p, inp["x"], inp["logits"], pgu, pd, pbgu, pbd, saved, dy,
+                                    yp=yp, ws=ws)
+    for _ in range(max(2, args.warmup // 4)):
+        fn()
+    torch.cuda.synchronize()
+    n = max(3, args.steps // 2)
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / n
+    N = int(disp["offsets"][-1].item())
+    flops = 16 * N * wl.H * wl.I
+    return {"ms": round(sec * 1e3, 4), "calls": n, "gemm_tflops": round(flops / sec / 1e12, 1),
+            "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 4),
+            "workspace_bytes": int(ws.numel())}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -315,6 +351,9 @@ def main():
     per_stage = {s: dict(us=round(stage_ms[s] * 1e3, 2),
                          **{k: v for k, v in roofline_of(s, alg, stage_ms[s] / 1e3, wl.dtype).items()
                             if k in ("bound", "achieved", "unit", "frac")}) for s in stages}
+    backward = None
+    if args.backward:
+        backward = time_backward(args, moe, p, wl, inp, pgu, pd, routing, disp, yp, dev)
     layer_calls = None
     if args.chunk_tokens > 0:
         layer_calls = time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev)
@@ -329,6 +368,8 @@ def main():
     }
     if layer_calls is not None:
         out["layer_calls"] = layer_calls
+    if backward is not None:
+        out["backward"] = backward
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_seconds, wr, groups)
     print(json.dumps(out), flush=True)

@@ -29,7 +29,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
 MOE_F32, MOE_BF16, MOE_FP8 = 0, 1, 2
 QBLOCK = 32  # elements per UE8M0 scale
-OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER, OP_ROUTER = range(6)
+OP_ROUTE, OP_DISPATCH, OP_FFN, OP_COMBINE, OP_LAYER, OP_ROUTER, OP_BACKWARD = range(7)
 W_GATE_UP, W_DOWN = 0, 1
 
 EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_packed_bytes",
@@ -37,7 +37,7 @@ EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_pa
            "moe_expert_gate_up_gather",
            "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
            "moe_route_grouped", "moe_router", "moe_layer_chunked_workspace_bytes",
-           "moe_layer_chunked")
+           "moe_layer_chunked", "moe_pack_weights_backward", "moe_layer_backward")
 
 
 class MoeError(RuntimeError):
@@ -49,6 +49,16 @@ class MoeError(RuntimeError):
 class MoeSharedExpert(ctypes.Structure):
     _fields_ = [("I", ctypes.c_int32), ("packed_gate_up", ctypes.c_void_p),
                 ("packed_down", ctypes.c_void_p)]
+
+
+class MoeSavedRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_ids", "topk_w", "offsets", "row_token", "slot_to_row")]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("dx", "dw_gate", "dw_up", "dw_down", "dlogits", "dtopk_w", "dw_router")]
 
 
 class MoeProblem(ctypes.Structure):
@@ -84,6 +94,10 @@ def _load() -> ctypes.CDLL:
         "moe_router": (ctypes.c_int, [PP, P, P, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P,
                                       sz, P]),
         "moe_layer_chunked_workspace_bytes": (sz, [PP, ctypes.c_int32, ctypes.c_int32]),
+        "moe_pack_weights_backward": (ctypes.c_int, [PP, P, P, P, P, P, P]),
+        "moe_layer_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P,
+                                              ctypes.POINTER(MoeSavedRouting), P, P,
+                                              ctypes.POINTER(MoeGrads), P, sz, P]),
         "moe_layer_chunked": (ctypes.c_int, [PP, P, P, P, P, ctypes.POINTER(MoeSharedExpert),
                                              ctypes.c_int32, P, P, sz, P, P]),
     }
@@ -427,6 +441,52 @@ def layer_chunked(p: Problem, x, logits, packed_gate_up, packed_down, chunk_toke
           _ptr(packed_down), None if sh is None else ctypes.byref(sh), int(chunk_tokens), _ptr(y),
           _ptr(ws), ws.numel(), _stream(), aux)
     return y
+
+
+def pack_weights_backward(p: Problem, w_gate, w_up, w_down):
+    """One-time packing of the backward operands ([W_gate | W_up]^T, W_down^T) from the
+    natural bf16 weights; returns (packed_bwd_gate_up, packed_bwd_down)."""
+    _need(w_gate, "w_gate", (p.E, p.H, p.I), torch.bfloat16)
+    _need(w_up, "w_up", (p.E, p.H, p.I), torch.bfloat16)
+    _need(w_down, "w_down", (p.E, p.I, p.H), torch.bfloat16)
+    dev = w_gate.device
+    pgu = _empty((p.packed_bytes(W_GATE_UP),), torch.uint8, dev)
+    pd = _empty((p.packed_bytes(W_DOWN),), torch.uint8, dev)
+    c = p.c()
+    _call("moe_pack_weights_backward", ctypes.byref(c), _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+          _ptr(pgu), _ptr(pd), _stream())
+    return pgu, pd
+
+
+def layer_backward(p: Problem, x, logits, packed_gate_up, packed_down, packed_bwd_gate_up,
+                   packed_bwd_down, routing, dy, yp=None, w_router=None, ws=None):
+    """Gradients of the layer (see moe_layer_backward).  routing: the forward's topk_ids,
+    topk_w, offsets, row_token, slot_to_row (a dict); yp: the forward's expert outputs or
+    None (recomputed).  Returns dict(dx, dw_gate, dw_up, dw_down, dlogits, dtopk_w[,
+    dw_router])."""
+    _need(x, "x", (p.T, p.H), torch.bfloat16)
+    _need(dy, "dy", (p.T, p.H), torch.bfloat16)
+    if yp is not None:
+        _need(yp, "yp", (p.T * p.k, p.H), torch.bfloat16)
+    dev = x.device
+    f32 = torch.float32
+    g = dict(dx=_empty((p.T, p.H), torch.bfloat16, dev),
+             dw_gate=_empty((p.E, p.H, p.I), f32, dev), dw_up=_empty((p.E, p.H, p.I), f32, dev),
+             dw_down=_empty((p.E, p.I, p.H), f32, dev), dlogits=_empty((p.T, p.E), f32, dev),
+             dtopk_w=_empty((p.T, p.k), f32, dev))
+    if w_router is not None:
+        _need(w_router, "w_router", (p.E, p.H), torch.bfloat16)
+        g["dw_router"] = _empty((p.E, p.H), f32, dev)
+    sv = MoeSavedRouting(*(routing[n].data_ptr() for n in
+                           ("topk_ids", "topk_w", "offsets", "row_token", "slot_to_row")))
+    gr = MoeGrads(*((g[n].data_ptr() if n in g else None) for n in
+                    ("dx", "dw_gate", "dw_up", "dw_down", "dlogits", "dtopk_w", "dw_router")))
+    ws = workspace(p, OP_BACKWARD, dev) if ws is None else ws
+    c = p.c()
+    _call("moe_layer_backward", ctypes.byref(c), _ptr(x), _ptr(logits), _ptr(w_router),
+          _ptr(packed_gate_up), _ptr(packed_down), _ptr(packed_bwd_gate_up), _ptr(packed_bwd_down),
+          ctypes.byref(sv), _ptr(yp), _ptr(dy), ctypes.byref(gr), _ptr(ws), ws.numel(), _stream())
+    return g
 
 
 def routing_buffers(p: Problem, device="cuda"):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "combine.hip", "pack.hip", "ffn_bf16.hip",
-           "ffn_f32.hip", "quant_fp8.hip", "ffn_fp8.hip"]
+           "ffn_f32.hip", "quant_fp8.hip", "ffn_fp8.hip", "backward.hip"]
 NO_CONTRACT = {"route.hip", "dispatch.hip"}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

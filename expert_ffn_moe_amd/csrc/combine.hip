@@ -21,7 +21,7 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
     rows[threadIdx.x] = s2r[(size_t)t * k + threadIdx.x];
-    wt[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    wt[threadIdx.x] = w ? w[(size_t)t * k + threadIdx.x] : 1.0f;  // NULL: unit weights
   }
   __syncthreads();
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
   const int t = blockIdx.x;
   if (threadIdx.x < k) {
     rows[threadIdx.x] = s2r[(size_t)t * k + threadIdx.x];
-    wt[threadIdx.x] = w[(size_t)t * k + threadIdx.x];
+    wt[threadIdx.x] = w ? w[(size_t)t * k + threadIdx.x] : 1.0f;  // NULL: unit weights
   }
   __syncthreads();
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {

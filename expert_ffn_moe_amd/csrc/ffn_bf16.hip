@@ -462,6 +462,35 @@ hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32
   return hipGetLastError();
 }
 
+// A plain grouped GEMM (the down projection's kernels) with any K and N: out[r] =
+// A[r] B[e] (rows through row_token if not NULL), B packed like the down weights
+// ([e][n32][k16] blocks), bf16 out.  The backward pass's data-gradient GEMMs.
+hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
+                            const int32_t* offsets, const void* packed_b, void* out, int K,
+                            int Nout, bool decode, hipStream_t s) {
+  const int nf32 = Nout / 32;
+  if (decode) {
+    if (row_token)
+      hipLaunchKernelGGL((decode_kernel<false, true>), dim3(div_up(nf32 / 2, 4), E), dim3(256), 0,
+                         s, (const uint16_t*)A, row_token, offsets, (const uint16_t*)packed_b,
+                         (uint16_t*)out, K, Nout);
+    else
+      hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), E), dim3(256),
+                         0, s, (const uint16_t*)A, nullptr, offsets, (const uint16_t*)packed_b,
+                         (uint16_t*)out, K, Nout);
+  } else {
+    if (row_token)
+      hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(persistent_grid()), dim3(kThreads),
+                         0, s, (const uint16_t*)A, row_token, offsets, E,
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout);
+    else
+      hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()),
+                         dim3(kThreads), 0, s, (const uint16_t*)A, nullptr, offsets, E,
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
                             const void* packed_d, void* yp, bool decode, hipStream_t s) {
   if (decode) {

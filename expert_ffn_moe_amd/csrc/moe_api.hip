@@ -172,6 +172,57 @@ RouterScratch carve_router(Carve& c, const moe_problem& p) {
   return r;
 }
 
+// ---- backward pass scratch: bf16 row buffers of the layout, their padded transposes, the
+// router's parts.
+bool backward_supported(const moe_problem& p, bool router) {
+  return p.act_dtype == MOE_BF16 && p.w_dtype == MOE_BF16 && p.H % 128 == 0 &&
+         p.H <= 8192 && (!router || p.E % 64 == 0);
+}
+bool router_bwd_ok(const moe_problem& p) { return p.E % 64 == 0; }
+
+struct BwdScratch {
+  float* dw;       // d topk_w when the caller does not want it
+  void *dyp, *da, *gu, *dgu, *a, *dxp, *yp;
+  FfnScratch ffn;  // the yp recompute's intermediate
+  int32_t* poff;
+  int64_t npad;    // row stride of the transposes
+  void *xT, *aT, *dypT, *dguT;
+  // router
+  void *dl16, *dxr, *wr_packed, *dlT, *xTf;
+  int32_t *roff, *rpoff;
+  int64_t tpad;
+};
+BwdScratch carve_backward(Carve& c, const moe_problem& p, bool router) {
+  const size_t tk = (size_t)p.T * p.k;
+  BwdScratch B{};
+  B.npad = (int64_t)((tk + 16 * (size_t)p.E + 15) & ~(size_t)15);
+  B.dw = c.take<float>(tk);
+  B.dyp = c.take<uint16_t>(tk * p.H);
+  B.da = c.take<uint16_t>(tk * p.I);
+  B.gu = c.take<uint16_t>(tk * 2 * p.I);
+  B.dgu = c.take<uint16_t>(tk * 2 * p.I);
+  B.a = c.take<uint16_t>(tk * p.I);
+  B.dxp = c.take<uint16_t>(tk * p.H);
+  B.yp = c.take<uint16_t>(tk * p.H);
+  B.ffn = carve_ffn(c, p);
+  B.poff = c.take<int32_t>((size_t)p.E + 1);
+  B.xT = c.take<uint16_t>((size_t)p.H * B.npad);
+  B.aT = c.take<uint16_t>((size_t)p.I * B.npad);
+  B.dypT = c.take<uint16_t>((size_t)p.H * B.npad);
+  B.dguT = c.take<uint16_t>((size_t)2 * p.I * B.npad);
+  if (router) {
+    B.tpad = (int64_t)(((size_t)p.T + 15) & ~(size_t)15);
+    B.dl16 = c.take<uint16_t>((size_t)p.T * p.E);
+    B.dxr = c.take<uint16_t>((size_t)p.T * p.H);
+    B.wr_packed = c.take<uint16_t>((size_t)p.E * p.H);
+    B.roff = c.take<int32_t>(2);
+    B.rpoff = c.take<int32_t>(2);
+    B.dlT = c.take<uint16_t>((size_t)p.E * B.tpad);
+    B.xTf = c.take<uint16_t>((size_t)p.H * B.tpad);
+  }
+  return B;
+}
+
 // Every entry point carves its workspace with the same function that sizes it here.
 size_t ws_bytes_of(const moe_problem& p, int op) {
   Carve c(nullptr);
@@ -185,6 +236,10 @@ size_t ws_bytes_of(const moe_problem& p, int op) {
       break;
     case MOE_OP_DISPATCH:
       carve_rank(c, p, false);
+      break;
+    case MOE_OP_BACKWARD:
+      if (!backward_supported(p, false)) return 0;
+      carve_backward(c, p, router_bwd_ok(p));
       break;
     case MOE_OP_FFN:
       carve_ffn(c, p);
@@ -547,6 +602,111 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if (err == hipSuccess)
     err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, ffn_use_decode(*p), s);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, nullptr, y, s);
+  return status_of(err);
+}
+
+int moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up,
+                              const void* w_down, void* packed_bwd_gate_up,
+                              void* packed_bwd_down, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!backward_supported(*p, false)) return MOE_ERR_UNSUPPORTED;
+  if (!w_gate || !w_up || !w_down || !packed_bwd_gate_up || !packed_bwd_down)
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(packed_bwd_gate_up) || !aligned16(packed_bwd_down)) return MOE_ERR_INVALID_ARG;
+  return status_of(launch_pack_backward(*p, w_gate, w_up, w_down, packed_bwd_gate_up,
+                                        packed_bwd_down, as_stream(stream)));
+}
+
+int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
+                       const void* w_router, const void* packed_gate_up,
+                       const void* packed_down, const void* packed_bwd_gate_up,
+                       const void* packed_bwd_down, const moe_saved_routing* saved,
+                       const void* yp, const void* dy, const moe_grads* grads, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!backward_supported(*p, w_router != nullptr)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !packed_gate_up || !packed_bwd_gate_up || !packed_bwd_down || !saved || !dy ||
+      !grads)
+    return MOE_ERR_INVALID_ARG;
+  if (!saved->topk_ids || !saved->topk_w || !saved->offsets || !saved->row_token ||
+      !saved->slot_to_row)
+    return MOE_ERR_INVALID_ARG;
+  if (!grads->dx || !grads->dw_gate || !grads->dw_up || !grads->dw_down || !grads->dlogits ||
+      (w_router && !grads->dw_router) || (!p->renormalize && !logits) ||
+      (!yp && !packed_down))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(grads->dx) || (yp && !aligned16(yp)) ||
+      (w_router && !aligned16(w_router)))
+    return MOE_ERR_INVALID_ARG;
+  if ((st = check_ws(p, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
+  Carve c(ws);
+  BwdScratch B = carve_backward(c, *p, router_bwd_ok(*p));
+  if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
+  hipStream_t s = as_stream(stream);
+  const moe_saved_routing& R = *saved;
+  const bool dec = ffn_use_decode(*p);
+  const int H = p->H, I = p->I, E = p->E;
+  const int64_t tk = (int64_t)p->T * p->k;
+  float* dw = grads->dtopk_w ? grads->dtopk_w : B.dw;
+  hipError_t err = hipSuccess;
+  // the forward's expert outputs, if not saved
+  if (!yp) {
+    err = run_gate_up(*p, x, R.row_token, R.offsets, packed_gate_up, B.ffn.a, B.ffn, dec, s);
+    if (err == hipSuccess) err = run_down(*p, B.ffn.a, R.offsets, packed_down, B.yp, dec, s);
+    yp = B.yp;
+  }
+  // combine and routing backward
+  if (err == hipSuccess) err = launch_combine_bwd(*p, dy, yp, R.topk_w, R.slot_to_row, B.dyp, dw, s);
+  if (err == hipSuccess) err = launch_route_bwd(*p, logits, R.topk_ids, R.topk_w, dw, grads->dlogits, s);
+  // data gradients: da = dyp W_down^T; g|u recomputed; SwiGLU backward; dxp = dgu [Wg|Wu]^T
+  if (err == hipSuccess)
+    err = launch_gemm_bf16(E, B.dyp, nullptr, R.offsets, packed_bwd_down, B.da, H, I, dec, s);
+  if (err == hipSuccess)
+    err = launch_gemm_bf16(E, x, R.row_token, R.offsets, packed_gate_up, B.gu, H, 2 * I, dec, s);
+  if (err == hipSuccess) err = launch_swiglu_bwd(*p, B.gu, B.da, R.offsets, B.dgu, B.a, s);
+  if (err == hipSuccess)
+    err = launch_gemm_bf16(E, B.dgu, nullptr, R.offsets, packed_bwd_gate_up, B.dxp, 2 * I, H,
+                           dec, s);
+  // the router's path: dx_r = dlogits W_r (added in the sum below), dW_r = dlogits^T x
+  const void* dxr = nullptr;
+  if (w_router && err == hipSuccess) {
+    err = launch_f32_to_bf16(grads->dlogits, (int64_t)p->T * E, B.dl16, s);
+    if (err == hipSuccess) err = launch_one_expert_offsets(B.roff, p->T, s);
+    if (err == hipSuccess) err = launch_pack_plain(1, E, H, w_router, B.wr_packed, s);
+    if (err == hipSuccess)
+      err = launch_gemm_bf16(1, B.dl16, nullptr, B.roff, B.wr_packed, B.dxr, E, H,
+                             p->T <= 24, s);
+    if (err == hipSuccess) err = launch_pad_offsets(B.roff, 1, B.rpoff, s);
+    if (err == hipSuccess)
+      err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, p->T, E, B.tpad, B.dlT, s);
+    if (err == hipSuccess)
+      err = launch_transpose_pad(x, nullptr, B.roff, B.rpoff, 1, p->T, H, B.tpad, B.xTf, s);
+    if (err == hipSuccess)
+      err = launch_wgrad(B.dlT, B.xTf, B.rpoff, 1, E, H, B.tpad, false, grads->dw_router,
+                         nullptr, s);
+    dxr = B.dxr;
+  }
+  // dispatch backward: dx[t] = sum over kept slots of dxp rows (+ the router's path)
+  if (err == hipSuccess)
+    err = launch_combine(*p, B.dxp, nullptr, R.slot_to_row, dxr, grads->dx, s);
+  // weight gradients over each expert's rows
+  if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, B.poff, s);
+  if (err == hipSuccess)
+    err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, tk, H, B.npad, B.xT, s);
+  if (err == hipSuccess)
+    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, tk, I, B.npad, B.aT, s);
+  if (err == hipSuccess)
+    err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, tk, H, B.npad, B.dypT, s);
+  if (err == hipSuccess)
+    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, tk, 2 * I, B.npad, B.dguT,
+                               s);
+  if (err == hipSuccess)
+    err = launch_wgrad(B.aT, B.dypT, B.poff, E, I, H, B.npad, false, grads->dw_down, nullptr, s);
+  if (err == hipSuccess)
+    err = launch_wgrad(B.xT, B.dguT, B.poff, E, H, 2 * I, B.npad, true, grads->dw_gate,
+                       grads->dw_up, s);
   return status_of(err);
 }
 

@@ -55,6 +55,10 @@ struct RouterPlan {
   int split;  // slices of H (a divisor of H / 64)
 };
 bool router_supported(const moe_problem& p);
+// d logits [T, E] from d topk_w (0 on dropped slots); logits are read only without
+// renormalisation.
+hipError_t launch_route_bwd(const moe_problem& p, const float* logits, const int32_t* ids,
+                            const float* w, const float* dw, float* dl, hipStream_t s);
 RouterPlan router_plan(const moe_problem& p);
 hipError_t launch_router(const moe_problem& p, const void* x, const void* wr, int n_group,
                          int topk_group, float* part, float* logits, int32_t* ids, float* w,
@@ -90,9 +94,32 @@ hipError_t launch_combine(const moe_problem& p, const void* yp, const float* w,
 // off[0] = 0, off[1] = n (the layout of a one-expert problem over n rows).
 hipError_t launch_one_expert_offsets(int32_t* off, int n, hipStream_t s);
 
+// ---- backward.hip
+hipError_t launch_combine_bwd(const moe_problem& p, const void* dy, const void* yp,
+                              const float* w, const int32_t* slot_to_row, void* dyp, float* dw,
+                              hipStream_t s);
+hipError_t launch_swiglu_bwd(const moe_problem& p, const void* gu, const void* da,
+                             const int32_t* offsets, void* dgu, void* a, hipStream_t s);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s);
+// [rows, C] bf16 (rows through row_map if not NULL) -> [C, npad], each expert's rows at
+// columns poff[e] .., padding columns zeroed; C % 64 == 0.
+hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
+                                const int32_t* poff, int E, int64_t max_rows, int C,
+                                int64_t npad, void* dst, hipStream_t s);
+// out[e][m][n] = sum_k AT[m][k] BT[n][k] over expert e's padded columns (M % 64 == 0,
+// Ncols % 128 == 0).
+hipError_t launch_wgrad(const void* AT, const void* BT, const int32_t* poff, int E, int M,
+                        int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
+                        hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* in, int64_t n, void* out, hipStream_t s);
+
 // ---- pack.hip
 hipError_t launch_pack(const moe_problem& p, const void* wg, const void* wu, const void* wd,
                        void* packed_gu, void* packed_d, hipStream_t s);
+hipError_t launch_pack_backward(const moe_problem& p, const void* wg, const void* wu,
+                                const void* wd, void* packed_bwd_gu, void* packed_bwd_d,
+                                hipStream_t s);
+hipError_t launch_pack_plain(int E, int K, int N, const void* w, void* packed, hipStream_t s);
 
 // ---- ffn_bf16.hip / ffn_f32.hip
 // The decode-shaped kernels (few rows per expert) or the prefill ones: decided from the
@@ -105,6 +132,11 @@ hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32
                                bool decode, hipStream_t s);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
                             const void* packed_d, void* yp, bool decode, hipStream_t s);
+// Plain grouped GEMM out[r] = A[r or row_token[r]] B[e] with B packed like the down weights
+// (K % 64 == 0 for the prefill kernel, K % 32 for the decode one; Nout % 64 == 0).
+hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
+                            const int32_t* offsets, const void* packed_b, void* out, int K,
+                            int Nout, bool decode, hipStream_t s);
 hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32_t* row_token,
                               const int32_t* offsets, const float* wg, const float* wu, float* a,
                               hipStream_t s);

@@ -154,6 +154,74 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   select_token<EPL>(lv, E, k, renorm, n_group, topk_group, lane, (size_t)t * k, ids, w, keep);
 }
 
+// Gradient of the logits from the gradient of the routing weights (dw = 0 for dropped
+// slots); the selection itself carries none.  One wavefront per token.
+//   renormalised: dl_j = w_j (dw_j - sum_i w_i dw_i) on the k selected experts, 0 elsewhere
+//   plain softmax: dl_e = p_e ([e selected] dw_e - sum_i w_i dw_i), p the softmax over all E
+// (p recomputed with the routing's exponential; sums in slot / expert order, fp32).
+template <int EPL>
+__global__ __launch_bounds__(256) void route_bwd_kernel(const float* __restrict__ logits,
+                                                        const int32_t* __restrict__ ids,
+                                                        const float* __restrict__ w,
+                                                        const float* __restrict__ dw, int T,
+                                                        int E, int k, int renorm,
+                                                        float* __restrict__ dl) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // wave-uniform
+  const size_t o = (size_t)t * k;
+  float inner = 0.0f;
+  for (int j = 0; j < k; ++j) inner = inner + w[o + j] * dw[o + j];
+  float p[EPL], d[EPL];
+  if (renorm) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) p[i] = 0.0f, d[i] = 0.0f;
+  } else {
+    const float* row = logits + (size_t)t * E;
+    float lv[EPL];
+    float m = -3.402823466e38f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      lv[i] = e < E ? row[e] : -3.402823466e38f;
+      m = fmaxf(m, lv[i]);
+    }
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) m = fmaxf(m, __shfl_xor(m, sh, 64));
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      p[i] = (lane + 64 * i < E) ? route_exp(lv[i] - m) : 0.0f;
+      const int n = min(64, E - 64 * i);
+      for (int src = 0; src < n; ++src)
+        s = s + __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(p[i]), src));
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      p[i] = p[i] / s;
+      d[i] = -p[i] * inner;
+    }
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[o + j];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (lane + 64 * i == e)
+        d[i] = renorm ? w[o + j] * (dw[o + j] - inner) : d[i] + p[i] * dw[o + j];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i)
+    if (lane + 64 * i < E) dl[(size_t)t * E + lane + 64 * i] = d[i];
+}
+
+template <int EPL>
+hipError_t launch_route_bwd_t(const moe_problem& p, const float* logits, const int32_t* ids,
+                              const float* w, const float* dw, float* dl, hipStream_t s) {
+  hipLaunchKernelGGL(route_bwd_kernel<EPL>, dim3(div_up(p.T, 4)), dim3(256), 0, s, logits, ids,
+                     w, dw, p.T, p.E, p.k, p.renormalize, dl);
+  return hipGetLastError();
+}
+
 template <int EPL>
 hipError_t launch_route_t(const moe_problem& p, const float* logits, int S, int n_group,
                           int topk_group, float* logits_out, int32_t* ids, float* w,
@@ -312,6 +380,15 @@ hipError_t launch_router_gemm_t(const moe_problem& p, const RouterPlan& plan, co
 hipError_t launch_route(const moe_problem& p, const float* logits, int n_group, int topk_group,
                         int32_t* ids, float* w, uint8_t* keep, hipStream_t s) {
   return launch_select(p, logits, 1, n_group, topk_group, nullptr, ids, w, keep, s);
+}
+
+hipError_t launch_route_bwd(const moe_problem& p, const float* logits, const int32_t* ids,
+                            const float* w, const float* dw, float* dl, hipStream_t s) {
+  if (p.E <= 64) return launch_route_bwd_t<1>(p, logits, ids, w, dw, dl, s);
+  if (p.E <= 128) return launch_route_bwd_t<2>(p, logits, ids, w, dw, dl, s);
+  if (p.E <= 256) return launch_route_bwd_t<4>(p, logits, ids, w, dw, dl, s);
+  if (p.E <= 512) return launch_route_bwd_t<8>(p, logits, ids, w, dw, dl, s);
+  return launch_route_bwd_t<16>(p, logits, ids, w, dw, dl, s);
 }
 
 bool router_supported(const moe_problem& p) {

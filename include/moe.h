@@ -10,6 +10,7 @@
  *   moe_layer        all of the above on one stream
  *   moe_layer_chunked  the layer over chunks of tokens, layouts on a second stream,
  *                    optional shared expert
+ *   moe_layer_backward gradients of the layer (x, expert weights, logits, router)
  *
  * The pages describe the operations in prose; each declaration names the passage:
  *   [axolotl]  docs.axolotl.ai "integrations.expert_parallel.args", attribute table
@@ -91,7 +92,8 @@ typedef enum {
   MOE_OP_FFN = 2, /* moe_expert_ffn; FP8 problems: also moe_expert_gate_up(_gather) */
   MOE_OP_COMBINE = 3,
   MOE_OP_LAYER = 4,
-  MOE_OP_ROUTER = 5 /* moe_router: split-K partial logits (+ capacity scratch) */
+  MOE_OP_ROUTER = 5, /* moe_router: split-K partial logits (+ capacity scratch) */
+  MOE_OP_BACKWARD = 6 /* moe_layer_backward (with the router and the yp recompute) */
 } moe_op;
 
 typedef enum { MOE_W_GATE_UP = 0, MOE_W_DOWN = 1 } moe_weight_set;
@@ -325,6 +327,63 @@ int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
                       const void* packed_gate_up, const void* packed_down,
                       const moe_shared_expert* shared, int32_t chunk_tokens, void* y, void* ws,
                       size_t ws_bytes, void* stream, void* aux_stream);
+
+/* ---------------------------------------------------------------------------------
+ * Backward pass -- [axolotl] attribute table, row `expert_parallel_save_dispatch`: the
+ * backward reuses the forward's routing (top-k and split counts are always saved) and the
+ * dispatch rows (here: gathered again from x through the saved row_token).  Gradients of
+ * the forward above (route -> capacity -> layout -> SwiGLU experts -> combine) for an
+ * upstream gradient dy; the selection itself carries no gradient.
+ *
+ * moe_pack_weights_backward: the backward's operands, one-time like moe_pack_weights,
+ *   from the natural bf16 weights: packed_bwd_gate_up (moe_packed_bytes(p,
+ *   MOE_W_GATE_UP) bytes) holds [W_gate | W_up]^T, packed_bwd_down (moe_packed_bytes(p,
+ *   MOE_W_DOWN) bytes) holds W_down^T.
+ *
+ * moe_layer_backward:
+ *   x [T, H] bf16, logits [T, E] f32 (read only when p->renormalize == 0),
+ *   w_router [E, H] bf16 or NULL: the gate of moe_router (then dw_router is written and
+ *     dx includes the router's path),
+ *   packed_gate_up / packed_down: the forward's packed weights (packed_down is read only
+ *     when yp is NULL), packed_bwd_*: from moe_pack_weights_backward,
+ *   saved: the forward's routing outputs, yp [T*k, H] bf16: the forward's expert outputs
+ *     (moe_expert_down), or NULL to recompute them,
+ *   dy [T, H] bf16.
+ * Outputs (grads): dx [T, H] bf16; dw_gate, dw_up [E, H, I] and dw_down [E, I, H] f32
+ *   (zero for experts without rows); dlogits [T, E] f32; dtopk_w [T, k] f32 or NULL;
+ *   dw_router [E, H] f32 (with w_router).
+ * Arithmetic: bf16 operands, fp32 accumulation; the intermediate gradients (dyp, da,
+ *   [dg | du], dxp) and the recomputed g, u, a are stored in bf16.
+ * MOE_ERR_UNSUPPORTED unless act and weight dtypes are bf16, H % 128 == 0, H <= 8192 (and,
+ * with a router, E % 64 == 0).  Workspace: moe_workspace_bytes(p, MOE_OP_BACKWARD).
+ * --------------------------------------------------------------------------------- */
+typedef struct {
+  const int32_t* topk_ids;    /* [T, k] */
+  const float* topk_w;        /* [T, k] */
+  const int32_t* offsets;     /* [E + 1] */
+  const int32_t* row_token;   /* [T * k] */
+  const int32_t* slot_to_row; /* [T, k], -1 for dropped slots */
+} moe_saved_routing;
+
+typedef struct {
+  void* dx;         /* [T, H] bf16 */
+  float* dw_gate;   /* [E, H, I] */
+  float* dw_up;     /* [E, H, I] */
+  float* dw_down;   /* [E, I, H] */
+  float* dlogits;   /* [T, E] */
+  float* dtopk_w;   /* [T, k] or NULL */
+  float* dw_router; /* [E, H], with a router */
+} moe_grads;
+
+int moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up,
+                              const void* w_down, void* packed_bwd_gate_up,
+                              void* packed_bwd_down, void* stream);
+int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
+                       const void* w_router, const void* packed_gate_up,
+                       const void* packed_down, const void* packed_bwd_gate_up,
+                       const void* packed_bwd_down, const moe_saved_routing* saved,
+                       const void* yp, const void* dy, const moe_grads* grads, void* ws,
+                       size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -47,17 +47,18 @@ def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int =
 
     x [T, H], w_gate/w_up [E, H, I], w_down [E, I, H] (f32/f64, or bf16 as uint16);
     logits [T, E] f32 (the routing is recomputed from them exactly as in the forward).
-    experts: if given, the weight gradients are computed for these experts only (the
-    others are returned as zeros); tokens: if given, dx, dlogits and dtopk_w are computed
+    experts: if given, the weight gradients are computed for these experts only and
+    dw_gate / dw_up / dw_down hold just them, in that order ([len(experts), ...]); tokens: if given, dx, dlogits and dtopk_w are computed
     for these tokens only (rows of other tokens are evaluated only where a listed expert's
     weight gradient needs them; the other tokens' entries are left at zero).
     Returns dict(dx [T,H], dw_gate, dw_up [E,H,I], dw_down [E,I,H], dlogits [T,E],
     dtopk_w [T,k], yp [N,H], and dw_router [E,H] if w_router is given), fp64."""
     X = _f64(np.asarray(x))
-    Wg, Wu, Wd = _f64(np.asarray(w_gate)), _f64(np.asarray(w_up)), _f64(np.asarray(w_down))
+    # weights stay in their storage type; each expert's are widened when it is evaluated
+    Wg_s, Wu_s, Wd_s = np.asarray(w_gate), np.asarray(w_up), np.asarray(w_down)
     dY = _f64(np.asarray(dy))
     T, H = X.shape
-    E, _, I = Wg.shape
+    E, _, I = Wg_s.shape
     ids, w = route(np.asarray(logits, np.float32), k, renormalize)
     keep = capacity(ids, w, E, capacity_)
     lay = layout(ids, keep, E)
@@ -76,27 +77,29 @@ def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int =
     row_w[s2r[tt, jj]] = w[tt, jj].astype(np.float64)
 
     dX = np.zeros((T, H))
-    dWg = np.zeros((E, H, I))
-    dWu = np.zeros((E, H, I))
-    dWd = np.zeros((E, I, H))
+    slot = {int(e): i for i, e in enumerate(wsel)}  # weight-gradient slot of each expert
+    dWg = np.zeros((len(wsel), H, I))
+    dWu = np.zeros((len(wsel), H, I))
+    dWd = np.zeros((len(wsel), I, H))
     yp = np.zeros((N, H))
     dW = np.zeros((T, k))
     for e in range(E):
         r0, r1 = int(off[e]), int(off[e + 1])
         if r1 == r0:
             continue
-        if e in wsel:
+        if e in slot:
             rows = np.arange(r0, r1)
         else:
             rows = np.arange(r0, r1)[tsel[rt[r0:r1]]]
             if rows.size == 0:
                 continue
         xe = X[rt[rows]]
-        g = xe @ Wg[e]
-        u = xe @ Wu[e]
+        Wge, Wue, Wde = _f64(Wg_s[e]), _f64(Wu_s[e]), _f64(Wd_s[e])
+        g = xe @ Wge
+        u = xe @ Wue
         sg = _sigmoid(g)
         a = g * sg * u
-        ype = a @ Wd[e]
+        ype = a @ Wde
         yp[rows] = ype
         dyt = dY[row_t[rows]]
         dyp = row_w[rows, None] * dyt
@@ -105,16 +108,16 @@ def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int =
             t = row_t[r]
             j = int(np.nonzero(s2r[t] == r)[0][0])
             dW[t, j] = dwr[q]
-        da = dyp @ Wd[e].T
+        da = dyp @ Wde.T
         du = da * g * sg
         dg = da * u * sg * (1.0 + g * (1.0 - sg))
         tok = rt[rows]
         mine = tsel[tok]
-        np.add.at(dX, tok[mine], (dg @ Wg[e].T + du @ Wu[e].T)[mine])
-        if e in wsel:
-            dWd[e] = a.T @ dyp
-            dWg[e] = xe.T @ dg
-            dWu[e] = xe.T @ du
+        np.add.at(dX, tok[mine], (dg @ Wge.T + du @ Wue.T)[mine])
+        if e in slot:
+            dWd[slot[e]] = a.T @ dyp
+            dWg[slot[e]] = xe.T @ dg
+            dWu[slot[e]] = xe.T @ du
 
     # router: d logits from d w (dropped slots carry no gradient: dW is 0 there)
     dW[~tsel] = 0.0
