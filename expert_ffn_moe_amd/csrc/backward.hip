@@ -12,9 +12,9 @@
 // The data-gradient GEMMs run on the forward's grouped-GEMM kernels with operands packed for
 // the backward (W_down^T, the interleaved [W_gate | W_up]^T).  The weight gradients reduce
 // over each expert's rows: the row-major [rows, C] operands are transposed into [C, rows]
-// with every expert's rows padded to a multiple of 16 (zeros), so that the reduction
-// dimension is contiguous for both matrix-core operands, and a grouped GEMM per expert
-// accumulates in fp32.
+// with every expert's rows padded to a multiple of 64 (zeros), so that the reduction
+// dimension is contiguous for both matrix-core operands, and the prefill GEMM tile
+// (launch_wgrad_bf16) accumulates each expert's gradient in fp32.
 #include <algorithm>
 
 #include "bf16.h"
@@ -23,9 +23,6 @@
 
 namespace moe {
 namespace {
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -119,13 +116,14 @@ __global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict
   }
 }
 
-// poff[e] = sum over e' < e of roundup16(offsets[e' + 1] - offsets[e']), poff[E] the total
-// (E <= 1024, one block).
+// poff[e] = sum over e' < e of the count of e' rounded up to a multiple of gran, poff[E]
+// the total (E <= 1024, one block).
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets,
-                                                           int E, int32_t* __restrict__ poff) {
+                                                           int E, int gran,
+                                                           int32_t* __restrict__ poff) {
   __shared__ int s[1024];
   const int e = threadIdx.x;
-  const int c = e < E ? ((offsets[e + 1] - offsets[e] + 15) & ~15) : 0;
+  const int c = e < E ? (offsets[e + 1] - offsets[e] + gran - 1) / gran * gran : 0;
   s[e] = c;
   __syncthreads();
   for (int d = 1; d < 1024; d <<= 1) {
@@ -138,143 +136,59 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   if (e == E - 1) poff[E] = s[e];
 }
 
-// dst[c][poff[e] + r - offsets[e]] = src[row r][c] (src row = row_map[r] if row_map), for
-// the layout rows r < offsets[E]; 64 rows x 64 columns per block through LDS.
+// dst[c][q] for the padded columns q of a block: column q = poff[e] + i holds src row
+// offsets[e] + i (through row_map if given) while i < count_e, zeros after.  A block takes
+// 64 destination columns x 64 values of c: loads 64 source rows (128 contiguous bytes
+// each), stores 64 destination rows (128 contiguous bytes each) through LDS.
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
                                                             const int32_t* __restrict__ row_map,
                                                             const int32_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ poff,
                                                             int E, int C, int64_t npad,
                                                             uint16_t* __restrict__ dst) {
-  __shared__ uint16_t tile[64][64 + 8];
-  __shared__ int prow[64];
-  const int n = offsets[E];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  if (r0 >= n) return;  // block-uniform
+  __shared__ uint32_t tile[64][33];  // [destination column][pairs of c], padded row
+  __shared__ int srow[64];
+  const int q0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (q0 >= poff[E]) return;  // block-uniform
   const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, part = tid & 3;
-    const int r = r0 + rr;
-    if (r < n) {
-      const int64_t sr = row_map ? row_map[r] : r;
-      const uint4* p = reinterpret_cast<const uint4*>(src + sr * C + c0 + 16 * part);
-      const uint4 v0 = p[0], v1 = p[1];
-      uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        tile[rr][16 * part + 2 * i] = (uint16_t)(wv[i] & 0xFFFF);
-        tile[rr][16 * part + 2 * i + 1] = (uint16_t)(wv[i] >> 16);
-      }
-      if (part == 0) {
-        int lo = 0, hi = E;  // expert of row r: the largest e with offsets[e] <= r
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (offsets[mid] <= r) lo = mid; else hi = mid;
-        }
-        prow[rr] = poff[lo] + r - offsets[lo];
-      }
+  if (tid < 64) {
+    const int q = q0 + tid;
+    int lo = 0, hi = E;  // expert of column q: the largest e with poff[e] <= q
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (poff[mid] <= q) lo = mid; else hi = mid;
     }
+    const int r = offsets[lo] + (q - poff[lo]);
+    srow[tid] = r < offsets[lo + 1] ? (row_map ? row_map[r] : r) : -1;
   }
   __syncthreads();
-  const int cc = tid >> 2, part = tid & 3;
-  uint16_t* d = dst + (int64_t)(c0 + cc) * npad;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int rr = 16 * part + i;
-    if (r0 + rr < n) d[prow[rr]] = tile[rr][cc];
-  }
-}
-
-// Zeros in the padding columns [poff[e] + count_e, poff[e + 1]) of every row c < C.
-__global__ __launch_bounds__(256) void zero_pad_kernel(const int32_t* __restrict__ offsets,
-                                                       const int32_t* __restrict__ poff, int C,
-                                                       int64_t npad, uint16_t* __restrict__ dst) {
-  const int e = blockIdx.x;
-  const int c0 = poff[e] + offsets[e + 1] - offsets[e], c1 = poff[e + 1];
-  const int w = c1 - c0;  // < 16
-  if (w <= 0) return;
-  for (int q = threadIdx.x; q < C * w; q += blockDim.x) {
-    const int c = q / w;
-    dst[(int64_t)c * npad + c0 + (q - c * w)] = 0;
-  }
-}
-
-// Weight gradient of every expert: out[e][m][n] = sum over its (padded) rows k of
-// AT[m][k] BT[n][k], fp32 (rows m >= M of the last tile are computed on clamped operands
-// and not stored).  A block of 4 wavefronts takes a 128 x 128 tile of one expert,
-// each wavefront 64 x 64 (2 x 2 accumulators of 32x32x16 bf16 MFMAs), operands loaded
-// straight from memory (both have the reduction dimension contiguous).  gu_split: the n
-// dimension is the interleaved gate|up one (2I): columns go to out (gate) or out2 (up),
-// each [E][M][I].
-__global__ __launch_bounds__(256) void wgrad_kernel(const uint16_t* __restrict__ AT,
-                                                    const uint16_t* __restrict__ BT,
-                                                    const int32_t* __restrict__ poff, int M,
-                                                    int Ncols, int64_t npad, int gu_split,
-                                                    float* __restrict__ out,
-                                                    float* __restrict__ out2) {
-  const int e = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int mb = blockIdx.x * 128 + (wave & 1) * 64;
-  const int nb = blockIdx.y * 128 + (wave >> 1) * 64;
-  const int k0 = poff[e], k1 = poff[e + 1];
-  const uint16_t* ap[2];
-  const uint16_t* bp[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    ap[i] = AT + (int64_t)min(mb + 32 * i + (lane & 31), M - 1) * npad + 8 * (lane >> 5);
-    bp[i] = BT + (int64_t)(nb + 32 * i + (lane & 31)) * npad + 8 * (lane >> 5);
-  }
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) acc[i][0] = acc[i][1] = f32x16_t{};
-  if (k1 > k0) {
-    uint4 a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = *(const uint4*)(ap[i] + k0);
-      b[i] = *(const uint4*)(bp[i] + k0);
+  {
+    const int j = tid >> 2, part = tid & 3;  // column j, values 16 part .. + 15
+    const int r = srow[j];
+    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+    if (r >= 0) {
+      const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)r * C + c0 + 16 * part);
+      v0 = p[0];
+      v1 = p[1];
     }
-    for (int k = k0; k < k1; k += 16) {
-      const int kn = min(k + 16, k1 - 16);  // the last step reloads its own operands
-      uint4 an[2], bn[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        an[i] = *(const uint4*)(ap[i] + kn);
-        bn[i] = *(const uint4*)(bp[i] + kn);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a[i]), __builtin_bit_cast(bf16x8_t, b[j]), acc[i][j],
-              0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = an[i];
-        b[i] = bn[i];
-      }
-    }
+    uint32_t* t = &tile[j][8 * part];
+    t[0] = v0.x; t[1] = v0.y; t[2] = v0.z; t[3] = v0.w;
+    t[4] = v1.x; t[5] = v1.y; t[6] = v1.z; t[7] = v1.w;
   }
-  // accumulator element q of lane l: row 8 (q / 4) + 4 (l / 32) + q % 4, column l % 32
-  const int I = Ncols / 2;
+  __syncthreads();
+  {
+    const int cc = tid >> 2, part = tid & 3;  // value c0 + cc, columns 16 part .. + 15
+    uint32_t w[8];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int m = mb + 32 * i + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3);
-        const int n = nb + 32 * j + (lane & 31);
-        if (m >= M) continue;
-        if (!gu_split) {
-          out[((int64_t)e * M + m) * Ncols + n] = acc[i][j][q];
-        } else {
-          const int blk = n >> 6, jj = n & 63;
-          float* o = jj < 32 ? out : out2;
-          o[((int64_t)e * M + m) * I + 32 * blk + (jj & 31)] = acc[i][j][q];
-        }
-      }
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t a = tile[16 * part + 2 * i][cc >> 1], b = tile[16 * part + 2 * i + 1][cc >> 1];
+      const int sh = 16 * (cc & 1);
+      w[i] = ((a >> sh) & 0xFFFF) | (((b >> sh) & 0xFFFF) << 16);
+    }
+    uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)(c0 + cc) * npad + q0 + 16 * part);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
 }
 
 __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restrict__ in,
@@ -307,28 +221,18 @@ hipError_t launch_swiglu_bwd(const moe_problem& p, const void* gu, const void* d
   return hipGetLastError();
 }
 
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s) {
-  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, poff);
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* poff,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(pad_offsets_kernel, dim3(1), dim3(1024), 0, s, offsets, E, gran, poff);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
-                                const int32_t* poff, int E, int64_t max_rows, int C,
-                                int64_t npad, void* dst, hipStream_t s) {
-  const dim3 grid((unsigned)div_up64(max_rows, 64), (unsigned)(C / 64));
+                                const int32_t* poff, int E, int C, int64_t npad, void* dst,
+                                hipStream_t s) {
+  const dim3 grid((unsigned)(npad / 64), (unsigned)(C / 64));
   hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, row_map,
                      offsets, poff, E, C, npad, (uint16_t*)dst);
-  hipLaunchKernelGGL(zero_pad_kernel, dim3(E), dim3(256), 0, s, offsets, poff, C, npad,
-                     (uint16_t*)dst);
-  return hipGetLastError();
-}
-
-hipError_t launch_wgrad(const void* AT, const void* BT, const int32_t* poff, int E, int M,
-                        int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
-                        hipStream_t s) {
-  const dim3 grid(div_up(M, 128), Ncols / 128, E);
-  hipLaunchKernelGGL(wgrad_kernel, grid, dim3(256), 0, s, (const uint16_t*)AT,
-                     (const uint16_t*)BT, poff, M, Ncols, npad, gu_split ? 1 : 0, out, out2);
   return hipGetLastError();
 }
 

@@ -54,9 +54,17 @@ struct TileArgs {
   const uint16_t* b0;    // this wavefront's first operand column (lane offset applied)
   const uint16_t* b1;    // second operand column
   uint16_t* out;         // output row row0, column col0 (row stride Nout)
+  float* outf;           // weight gradients: fp32 output row row0, column col0
+  float* outf2;          // ... its up half when the columns are the interleaved gate|up
   int K, Nout, rows, wave, lane, act;
+  int nst;               // stages of 64 along K
+  int col0;              // weight gradients: the wavefront's first output column
+  int gu_split;
   int fbase[4];          // LDS index of this lane's fragment piece, per k-step, m32 = 0
 };
+
+// Tile epilogues: SwiGLU to bf16 `a`, bf16 GEMM output, fp32 weight gradient.
+enum TileMode { kModeGateUp = 0, kModeDown = 1, kModeWgrad = 2 };
 
 // LDS activation stage: 128 rows x 64 k bf16, row-major, 16-byte chunk c of row r stored
 // at chunk position c ^ f(r), f(r) = ((r >> 1) ^ (r << 2)) & 7.  f takes 8 distinct values
@@ -72,7 +80,9 @@ __device__ __forceinline__ int a_slot(int r, int c) {
 // k-step KK of a stage: MFMAs with activation fragments `a` and ring slot KK, then the
 // slot is refilled with operand k-step j_next; the next k-step's fragments are read
 // from LDS first so that their latency hides behind these MFMAs.
-template <int NM, int BUF, int KK>
+// BSTRIDE: elements between the operand pieces of consecutive k-steps (a packed weight
+// block: 512; a row-major [N][K] operand: 16).
+template <int NM, int BUF, int KK, int BSTRIDE>
 __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                       bf16x8_t (&a)[4], const u32x4 (*lds)[1024],
                                       const TileArgs& t, int j_next) {
@@ -90,7 +100,7 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
     acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv0, acc[m][0], 0, 0, 0);
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv1, acc[m][1], 0, 0, 0);
   }
-  const size_t o = (size_t)j_next * kOperandElems;
+  const size_t o = (size_t)j_next * BSTRIDE;
   bring[KK][0] = *(const u32x4*)(t.b0 + o);
   bring[KK][1] = *(const u32x4*)(t.b1 + o);
   if (KK < 3) {
@@ -102,7 +112,7 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
 
 // One stage (4 k-steps of 16) from LDS buffer BUF.  Activations are loaded two stages
 // ahead into register set BUF and stored to LDS one stage ahead.
-template <int NM, int BUF>
+template <int NM, int BUF, int BSTRIDE>
 __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                        u32x4 (&aset0)[2], u32x4 (&aset1)[2],
                                        u32x4 (*lds)[1024], const uint16_t* const (&ag)[2],
@@ -125,10 +135,10 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
   }
   // ring slots are refilled with the next stage's operands
   const int jn = 4 * (s + 1), jmax = 4 * nst - 1;
-  kstep<NM, BUF, 0>(acc, bring, a, lds, t, min(jn + 0, jmax));
-  kstep<NM, BUF, 1>(acc, bring, a, lds, t, min(jn + 1, jmax));
-  kstep<NM, BUF, 2>(acc, bring, a, lds, t, min(jn + 2, jmax));
-  kstep<NM, BUF, 3>(acc, bring, a, lds, t, min(jn + 3, jmax));
+  kstep<NM, BUF, 0, BSTRIDE>(acc, bring, a, lds, t, min(jn + 0, jmax));
+  kstep<NM, BUF, 1, BSTRIDE>(acc, bring, a, lds, t, min(jn + 1, jmax));
+  kstep<NM, BUF, 2, BSTRIDE>(acc, bring, a, lds, t, min(jn + 2, jmax));
+  kstep<NM, BUF, 3, BSTRIDE>(acc, bring, a, lds, t, min(jn + 3, jmax));
   // stage s + 1 (loaded at the start of stage s - 1) into the other buffer
   if constexpr (BUF == 0) {
     lds[1][lslot[0]] = aset1[0];
@@ -140,10 +150,11 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
   __syncthreads();
 }
 
-// One work item: 128 rows x (this wavefront's two operand columns).
-template <bool GATE_UP, bool GATHER>
+// One work item: 128 rows x (this wavefront's two operand columns), t.nst >= 1 stages.
+template <int MODE, bool GATHER, int BSTRIDE>
 __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[1024]) {
-  const int nst = t.K / 64;
+  constexpr bool GATE_UP = MODE == kModeGateUp;
+  const int nst = t.nst;
   const int lane = t.lane, wave = t.wave;
   // activation loader: the p-th load of wavefront w covers rows 64p + 8w .. + 7, lane L
   // taking chunk L % 8 of row L / 8: whole 128-byte lines
@@ -170,7 +181,7 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   aset1[1] = *(const u32x4*)(ag[1] + s1);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) {
-    const size_t o = (size_t)min(q, 4 * nst - 1) * kOperandElems;
+    const size_t o = (size_t)min(q, 4 * nst - 1) * BSTRIDE;
     bring[q][0] = *(const u32x4*)(t.b0 + o);
     bring[q][1] = *(const u32x4*)(t.b1 + o);
   }
@@ -179,14 +190,41 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   __syncthreads();
   if (t.rows > 64) {  // block-uniform: a tile with at most 64 live rows skips the others
     for (int s0 = 0; s0 < nst; s0 += 2) {
-      kstage<4, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
-      if (s0 + 1 < nst) kstage<4, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+      kstage<4, 0, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      if (s0 + 1 < nst)
+        kstage<4, 1, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
   } else {
     for (int s0 = 0; s0 < nst; s0 += 2) {
-      kstage<2, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
-      if (s0 + 1 < nst) kstage<2, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+      kstage<2, 0, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      if (s0 + 1 < nst)
+        kstage<2, 1, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
+  }
+
+  if constexpr (MODE == kModeWgrad) {
+    // fp32 straight from the accumulators: for each register, the 32 lanes of a half
+    // wavefront write 32 consecutive floats of one row
+    if (!t.act) return;
+    const int col = t.col0 + (lane & 31);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (r >= t.rows) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int n = col + 32 * h;
+          if (!t.gu_split) {
+            t.outf[(size_t)r * t.Nout + n] = acc[m][h][i];
+          } else {  // interleaved gate|up columns: 64 b + j -> gate (j < 32) or up column 32 b + j % 32
+            float* o = (n & 32) ? t.outf2 : t.outf;
+            o[(size_t)r * (t.Nout / 2) + 32 * (n >> 6) + (n & 31)] = acc[m][h][i];
+          }
+        }
+      }
+    return;
   }
 
   // Epilogue through LDS: per 32-row fragment, each wavefront writes its 32 x 32 (gate/up,
@@ -303,6 +341,7 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     TileArgs t;
     t.rows = min(kPrefillBM, offsets[e + 1] - row0);
     t.K = K;
+    t.nst = K / 64;
     t.Nout = Nout;
     t.wave = wave;
     // lane goes through an empty asm statement so that nothing derived from it is
@@ -334,8 +373,66 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     t.out = out + (size_t)row0 * Nout + col0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
-    prefill_tile<GATE_UP, GATHER>(t, lds_a);
+    prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER, kOperandElems>(t, lds_a);
   }
+}
+
+// ------------------------------------------------------------------------------------
+// Weight gradients of every expert (backward pass): out[e][m][n] = sum over the expert's
+// rows k of AT[m][k] BT[n][k], with AT [M][npad] and BT [Ncols][npad] bf16 row-major (the
+// reduction dimension contiguous; each expert's rows padded with zeros to a multiple of
+// 64 starting at poff[e]).  The prefill tile with the roles of the forward: tile rows =
+// 128 of M, a wavefront's two operand columns = 64 of Ncols (512 per block of 8
+// wavefronts), read from BT rows (consecutive k-steps 16 elements apart), K = the rows;
+// fp32 out.  gu_split: Ncols is the interleaved gate|up dimension, the columns go to out
+// (gate) and out2 (up), each [E][M][Ncols / 2].  Grid: (M / 128 rounded up, Ncols / 512
+// rounded up, E); experts without rows get zeros.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ BT,
+                  const int32_t* __restrict__ poff, int M, int Ncols, int npad, int gu_split,
+                  float* __restrict__ out, float* __restrict__ out2) {
+  __shared__ u32x4 lds_a[2][1024];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int e = blockIdx.z;
+  const int m0 = blockIdx.x * kPrefillBM;
+  const int k0 = poff[e], kn = poff[e + 1] - k0;
+  TileArgs t;
+  t.rows = min(kPrefillBM, M - m0);
+  t.K = npad;  // the A row stride
+  t.nst = kn / 64;
+  t.Nout = Ncols;
+  t.wave = wave;
+  t.lane = lane;
+  const int n0 = blockIdx.y * 64 * kWaves + wave * 64;
+  t.act = n0 < Ncols;
+  const int nc = min(n0, Ncols - 64);  // idle wavefronts keep valid (unstored) columns
+  t.col0 = nc;
+  t.gu_split = gu_split;
+  t.A = AT + (size_t)m0 * npad + k0;
+  t.rtok = nullptr;
+  t.b0 = BT + (size_t)(nc + (lane & 31)) * npad + k0 + 8 * (lane >> 5);
+  t.b1 = t.b0 + (size_t)32 * npad;
+  const size_t orow = (size_t)e * M + m0;
+  t.outf = out + orow * (gu_split ? Ncols / 2 : Ncols);
+  t.outf2 = gu_split ? out2 + orow * (Ncols / 2) : nullptr;
+  t.out = nullptr;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane & 31, 2 * kk + (lane >> 5));
+  if (t.nst > 0) {  // block-uniform
+    prefill_tile<kModeWgrad, false, 16>(t, lds_a);
+    return;
+  }
+  if (!t.act) return;
+  for (int r = 0; r < t.rows; ++r)
+    for (int h = 0; h < 2; ++h) {
+      const int n = nc + 32 * h + (lane & 31);
+      if (lane >= 32) continue;
+      if (!gu_split)
+        t.outf[(size_t)r * Ncols + n] = 0.0f;
+      else
+        ((n & 32) ? t.outf2 : t.outf)[(size_t)r * (Ncols / 2) + 32 * (n >> 6) + (n & 31)] = 0.0f;
+    }
 }
 
 // ------------------------------------------------------------------------------------
@@ -414,6 +511,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
 }
 
 }  // namespace
+
+hipError_t launch_wgrad_bf16(const void* AT, const void* BT, const int32_t* poff, int E, int M,
+                             int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
+                             hipStream_t s) {
+  const dim3 grid(div_up(M, kPrefillBM), div_up(Ncols, 64 * kWaves), E);
+  hipLaunchKernelGGL(wgrad_kernel, grid, dim3(kThreads), 0, s, (const uint16_t*)AT,
+                     (const uint16_t*)BT, poff, M, Ncols, (int)npad, gu_split ? 1 : 0, out, out2);
+  return hipGetLastError();
+}
 
 // Decode shape: few rows per expert on average.
 bool ffn_use_decode(const moe_problem& p) { return (int64_t)p.T * p.k <= (int64_t)24 * p.E; }

@@ -195,7 +195,7 @@ struct BwdScratch {
 BwdScratch carve_backward(Carve& c, const moe_problem& p, bool router) {
   const size_t tk = (size_t)p.T * p.k;
   BwdScratch B{};
-  B.npad = (int64_t)((tk + 16 * (size_t)p.E + 15) & ~(size_t)15);
+  B.npad = (int64_t)((tk + 64 * (size_t)p.E + 63) & ~(size_t)63);  // rows padded per expert
   B.dw = c.take<float>(tk);
   B.dyp = c.take<uint16_t>(tk * p.H);
   B.da = c.take<uint16_t>(tk * p.I);
@@ -211,7 +211,7 @@ BwdScratch carve_backward(Carve& c, const moe_problem& p, bool router) {
   B.dypT = c.take<uint16_t>((size_t)p.H * B.npad);
   B.dguT = c.take<uint16_t>((size_t)2 * p.I * B.npad);
   if (router) {
-    B.tpad = (int64_t)(((size_t)p.T + 15) & ~(size_t)15);
+    B.tpad = (int64_t)(((size_t)p.T + 63) & ~(size_t)63);
     B.dl16 = c.take<uint16_t>((size_t)p.T * p.E);
     B.dxr = c.take<uint16_t>((size_t)p.T * p.H);
     B.wr_packed = c.take<uint16_t>((size_t)p.E * p.H);
@@ -648,7 +648,6 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   const moe_saved_routing& R = *saved;
   const bool dec = ffn_use_decode(*p);
   const int H = p->H, I = p->I, E = p->E;
-  const int64_t tk = (int64_t)p->T * p->k;
   float* dw = grads->dtopk_w ? grads->dtopk_w : B.dw;
   hipError_t err = hipSuccess;
   // the forward's expert outputs, if not saved
@@ -678,35 +677,35 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
     if (err == hipSuccess)
       err = launch_gemm_bf16(1, B.dl16, nullptr, B.roff, B.wr_packed, B.dxr, E, H,
                              p->T <= 24, s);
-    if (err == hipSuccess) err = launch_pad_offsets(B.roff, 1, B.rpoff, s);
+    if (err == hipSuccess) err = launch_pad_offsets(B.roff, 1, 64, B.rpoff, s);
     if (err == hipSuccess)
-      err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, p->T, E, B.tpad, B.dlT, s);
+      err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, E, B.tpad, B.dlT, s);
     if (err == hipSuccess)
-      err = launch_transpose_pad(x, nullptr, B.roff, B.rpoff, 1, p->T, H, B.tpad, B.xTf, s);
+      err = launch_transpose_pad(x, nullptr, B.roff, B.rpoff, 1, H, B.tpad, B.xTf, s);
     if (err == hipSuccess)
-      err = launch_wgrad(B.dlT, B.xTf, B.rpoff, 1, E, H, B.tpad, false, grads->dw_router,
-                         nullptr, s);
+      err = launch_wgrad_bf16(B.dlT, B.xTf, B.rpoff, 1, E, H, B.tpad, false, grads->dw_router,
+                              nullptr, s);
     dxr = B.dxr;
   }
   // dispatch backward: dx[t] = sum over kept slots of dxp rows (+ the router's path)
   if (err == hipSuccess)
     err = launch_combine(*p, B.dxp, nullptr, R.slot_to_row, dxr, grads->dx, s);
   // weight gradients over each expert's rows
-  if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, B.poff, s);
+  if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, 64, B.poff, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, tk, H, B.npad, B.xT, s);
+    err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, H, B.npad, B.xT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, tk, I, B.npad, B.aT, s);
+    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, I, B.npad, B.aT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, tk, H, B.npad, B.dypT, s);
+    err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, H, B.npad, B.dypT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, tk, 2 * I, B.npad, B.dguT,
-                               s);
+    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, 2 * I, B.npad, B.dguT, s);
   if (err == hipSuccess)
-    err = launch_wgrad(B.aT, B.dypT, B.poff, E, I, H, B.npad, false, grads->dw_down, nullptr, s);
+    err = launch_wgrad_bf16(B.aT, B.dypT, B.poff, E, I, H, B.npad, false, grads->dw_down,
+                            nullptr, s);
   if (err == hipSuccess)
-    err = launch_wgrad(B.xT, B.dguT, B.poff, E, H, 2 * I, B.npad, true, grads->dw_gate,
-                       grads->dw_up, s);
+    err = launch_wgrad_bf16(B.xT, B.dguT, B.poff, E, H, 2 * I, B.npad, true, grads->dw_gate,
+                            grads->dw_up, s);
   return status_of(err);
 }
 

@@ -100,17 +100,14 @@ hipError_t launch_combine_bwd(const moe_problem& p, const void* dy, const void* 
                               hipStream_t s);
 hipError_t launch_swiglu_bwd(const moe_problem& p, const void* gu, const void* da,
                              const int32_t* offsets, void* dgu, void* a, hipStream_t s);
-hipError_t launch_pad_offsets(const int32_t* offsets, int E, int32_t* poff, hipStream_t s);
+// poff[e]: the exclusive scan of the counts rounded up to a multiple of gran (16 or 64).
+hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* poff,
+                              hipStream_t s);
 // [rows, C] bf16 (rows through row_map if not NULL) -> [C, npad], each expert's rows at
-// columns poff[e] .., padding columns zeroed; C % 64 == 0.
+// columns poff[e] .. (a multiple of 64), padding columns zeroed; C % 64 == 0, npad % 64 == 0.
 hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
-                                const int32_t* poff, int E, int64_t max_rows, int C,
-                                int64_t npad, void* dst, hipStream_t s);
-// out[e][m][n] = sum_k AT[m][k] BT[n][k] over expert e's padded columns (M % 64 == 0,
-// Ncols % 128 == 0).
-hipError_t launch_wgrad(const void* AT, const void* BT, const int32_t* poff, int E, int M,
-                        int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
-                        hipStream_t s);
+                                const int32_t* poff, int E, int C, int64_t npad, void* dst,
+                                hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, int64_t n, void* out, hipStream_t s);
 
 // ---- pack.hip
@@ -137,6 +134,11 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
 hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
                             const int32_t* offsets, const void* packed_b, void* out, int K,
                             int Nout, bool decode, hipStream_t s);
+// Weight gradients on the matrix cores: out[e][m][n] = sum_k AT[m][k] BT[n][k] over expert
+// e's rows [poff[e], poff[e + 1]) (a multiple of 64, zero-padded); Ncols % 64 == 0.
+hipError_t launch_wgrad_bf16(const void* AT, const void* BT, const int32_t* poff, int E, int M,
+                             int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
+                             hipStream_t s);
 hipError_t launch_gate_up_f32(const moe_problem& p, const float* xs, const int32_t* row_token,
                               const int32_t* offsets, const float* wg, const float* wu, float* a,
                               hipStream_t s);
