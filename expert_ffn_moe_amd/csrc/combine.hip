@@ -10,6 +10,9 @@
 namespace moe {
 namespace {
 
+// KMAX > 0: k <= KMAX, the k row loads of a vector are issued together before any of them
+// is used (the slot loop unrolled); KMAX = 0: any k, one slot at a time.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restrict__ yp,
                                                            const float* __restrict__ w,
                                                            const int32_t* __restrict__ s2r,
@@ -26,14 +29,31 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint4* __restri
   __syncthreads();
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int j = 0; j < k; ++j) {
-      const int r = rows[j];
-      if (r < 0) continue;
-      float f[8];
-      unpack8(yp[(size_t)r * nvec + v], f);
-      const float wj = wt[j];
+    if constexpr (KMAX > 0) {
+      uint4 rv[KMAX];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+      for (int j = 0; j < KMAX; ++j)
+        if (j < k && rows[j] >= 0) rv[j] = yp[(size_t)rows[j] * nvec + v];
+#pragma unroll
+      for (int j = 0; j < KMAX; ++j) {
+        if (j < k && rows[j] >= 0) {  // block-uniform
+          float f[8];
+          unpack8(rv[j], f);
+          const float wj = wt[j];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+        }
+      }
+    } else {
+      for (int j = 0; j < k; ++j) {
+        const int r = rows[j];
+        if (r < 0) continue;
+        float f[8];
+        unpack8(yp[(size_t)r * nvec + v], f);
+        const float wj = wt[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(wj, f[i], acc[i]);
+      }
     }
     if (shared) {
       float f[8];
@@ -95,8 +115,14 @@ hipError_t launch_combine(const moe_problem& p, const void* yp, const float* w,
   if (p.act_dtype == MOE_F32)
     hipLaunchKernelGGL(combine_f32_kernel, dim3(p.T), dim3(256), 0, s, (const float4*)yp, w,
                        slot_to_row, p.k, p.H / 4, (const float4*)shared, (float4*)y);
+  else if (p.k <= 4)
+    hipLaunchKernelGGL(combine_bf16_kernel<4>, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
+                       slot_to_row, p.k, p.H / 8, (const uint4*)shared, (uint4*)y);
+  else if (p.k <= 8)
+    hipLaunchKernelGGL(combine_bf16_kernel<8>, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
+                       slot_to_row, p.k, p.H / 8, (const uint4*)shared, (uint4*)y);
   else
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
+    hipLaunchKernelGGL(combine_bf16_kernel<0>, dim3(p.T), dim3(256), 0, s, (const uint4*)yp, w,
                        slot_to_row, p.k, p.H / 8, (const uint4*)shared, (uint4*)y);
   return hipGetLastError();
 }

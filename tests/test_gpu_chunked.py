@@ -172,3 +172,37 @@ def test_chunked_full_size_qwen3_with_shared_expert():
     rng = np.random.default_rng(7)
     tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 30, replace=False)]))
     check_shared(wl, 1536, 1024, tokens=tokens)
+
+
+def test_chunked_fp8_with_shared_expert():
+    """FP8 weights for the routed and the shared expert: y against the FP8 oracle (the
+    routed rows and the shared rows quantised exactly as the path does), normwise 2e-2."""
+    wl = Workload("chk_fp8_shared", T=300, H=256, E=8, k=2, I=128, capacity=0, dtype="fp8",
+                  logits="normal", seed=66)
+    I = 256
+    say(f"case {wl.name} shared I={I}")
+    m = moe()
+    p = m.Problem.of(wl)
+    inp = synth.make_inputs(wl, DEV)
+    pgu, pd = m.pack_weights(p, inp["w_gate"], inp["w_up"], inp["w_down"])
+    swg, swu, swd = shared_weights(wl, I, DEV)
+    spgu, spd = m.pack_weights(m.shared_problem(p, I), swg, swu, swd)
+    y = m.layer_chunked(p, inp["x"], inp["logits"], pgu, pd, 128, shared=(I, spgu, spd),
+                        aux_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    ids, w = oracle.route(host(inp["logits"]), p.k, p.renormalize)
+    lay = oracle.layout(ids, None, p.E)
+    N = lay["N"]
+    xh = host(inp["x"])
+    rexp = (np.searchsorted(lay["offsets"], np.arange(N), side="right") - 1).astype(np.int32)
+    xq, xs = oracle.quant_rows(xh[lay["row_token"][:N]])
+    wq = [oracle.quant_weights(host(inp[n])) for n in ("w_gate", "w_up", "w_down")]
+    yp = oracle.ffn_rows_fp8(xq, xs, rexp, *wq)
+    sq, ss = oracle.quant_rows(xh)
+    swq = [oracle.quant_weights(host(t)) for t in (swg, swu, swd)]
+    sh = oracle.ffn_rows_fp8(sq, ss, np.zeros(p.T, np.int32), *swq)
+    ref = oracle.combine(np.arange(p.T, dtype=np.int32), w, lay["slot_to_row"], yp, sh)
+    got = as_f64(host(y))
+    err, scale = np.abs(got - ref).max(), np.abs(ref).max()
+    say(f"  y: max err {err:.3e} of max|ref| {scale:.3e}")
+    assert err <= 2e-2 * scale
