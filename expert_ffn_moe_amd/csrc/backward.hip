@@ -140,6 +140,10 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
 // offsets[e] + i (through row_map if given) while i < count_e, zeros after.  A block takes
 // 64 destination columns x 64 values of c: loads 64 source rows (128 contiguous bytes
 // each), stores 64 destination rows (128 contiguous bytes each) through LDS.
+// PACKED: dst in matrix-core operand order instead (the weight-gradient GEMM's B operand):
+// 1 KiB blocks of 32 values of c x 16 columns q, ordered [c / 32][q / 16]; piece
+// (c % 32) + 32 h of a block holds columns 8 h .. + 7 of value c.
+template <bool PACKED>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
                                                             const int32_t* __restrict__ row_map,
                                                             const int32_t* __restrict__ offsets,
@@ -185,9 +189,17 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
       const int sh = 16 * (cc & 1);
       w[i] = ((a >> sh) & 0xFFFF) | (((b >> sh) & 0xFFFF) << 16);
     }
-    uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)(c0 + cc) * npad + q0 + 16 * part);
-    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    if constexpr (PACKED) {
+      const int c = c0 + cc;
+      uint4* blk = reinterpret_cast<uint4*>(dst) +
+                   ((int64_t)(c >> 5) * (npad >> 4) + (q0 >> 4) + part) * 64;
+      blk[c & 31] = make_uint4(w[0], w[1], w[2], w[3]);
+      blk[(c & 31) + 32] = make_uint4(w[4], w[5], w[6], w[7]);
+    } else {
+      uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)(c0 + cc) * npad + q0 + 16 * part);
+      d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+      d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    }
   }
 }
 
@@ -228,11 +240,15 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* 
 }
 
 hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
-                                const int32_t* poff, int E, int C, int64_t npad, void* dst,
-                                hipStream_t s) {
+                                const int32_t* poff, int E, int C, int64_t npad, bool packed,
+                                void* dst, hipStream_t s) {
   const dim3 grid((unsigned)(npad / 64), (unsigned)(C / 64));
-  hipLaunchKernelGGL(transpose_pad_kernel, grid, dim3(256), 0, s, (const uint16_t*)src, row_map,
-                     offsets, poff, E, C, npad, (uint16_t*)dst);
+  if (packed)
+    hipLaunchKernelGGL(transpose_pad_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src,
+                       row_map, offsets, poff, E, C, npad, (uint16_t*)dst);
+  else
+    hipLaunchKernelGGL(transpose_pad_kernel<false>, grid, dim3(256), 0, s, (const uint16_t*)src,
+                       row_map, offsets, poff, E, C, npad, (uint16_t*)dst);
   return hipGetLastError();
 }
 

@@ -80,9 +80,7 @@ __device__ __forceinline__ int a_slot(int r, int c) {
 // k-step KK of a stage: MFMAs with activation fragments `a` and ring slot KK, then the
 // slot is refilled with operand k-step j_next; the next k-step's fragments are read
 // from LDS first so that their latency hides behind these MFMAs.
-// BSTRIDE: elements between the operand pieces of consecutive k-steps (a packed weight
-// block: 512; a row-major [N][K] operand: 16).
-template <int NM, int BUF, int KK, int BSTRIDE>
+template <int NM, int BUF, int KK>
 __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                       bf16x8_t (&a)[4], const u32x4 (*lds)[1024],
                                       const TileArgs& t, int j_next) {
@@ -100,7 +98,7 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
     acc[m][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv0, acc[m][0], 0, 0, 0);
     acc[m][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], bv1, acc[m][1], 0, 0, 0);
   }
-  const size_t o = (size_t)j_next * BSTRIDE;
+  const size_t o = (size_t)j_next * kOperandElems;
   bring[KK][0] = *(const u32x4*)(t.b0 + o);
   bring[KK][1] = *(const u32x4*)(t.b1 + o);
   if (KK < 3) {
@@ -112,7 +110,7 @@ __device__ __forceinline__ void kstep(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRin
 
 // One stage (4 k-steps of 16) from LDS buffer BUF.  Activations are loaded two stages
 // ahead into register set BUF and stored to LDS one stage ahead.
-template <int NM, int BUF, int BSTRIDE>
+template <int NM, int BUF>
 __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRing][2],
                                        u32x4 (&aset0)[2], u32x4 (&aset1)[2],
                                        u32x4 (*lds)[1024], const uint16_t* const (&ag)[2],
@@ -135,10 +133,10 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
   }
   // ring slots are refilled with the next stage's operands
   const int jn = 4 * (s + 1), jmax = 4 * nst - 1;
-  kstep<NM, BUF, 0, BSTRIDE>(acc, bring, a, lds, t, min(jn + 0, jmax));
-  kstep<NM, BUF, 1, BSTRIDE>(acc, bring, a, lds, t, min(jn + 1, jmax));
-  kstep<NM, BUF, 2, BSTRIDE>(acc, bring, a, lds, t, min(jn + 2, jmax));
-  kstep<NM, BUF, 3, BSTRIDE>(acc, bring, a, lds, t, min(jn + 3, jmax));
+  kstep<NM, BUF, 0>(acc, bring, a, lds, t, min(jn + 0, jmax));
+  kstep<NM, BUF, 1>(acc, bring, a, lds, t, min(jn + 1, jmax));
+  kstep<NM, BUF, 2>(acc, bring, a, lds, t, min(jn + 2, jmax));
+  kstep<NM, BUF, 3>(acc, bring, a, lds, t, min(jn + 3, jmax));
   // stage s + 1 (loaded at the start of stage s - 1) into the other buffer
   if constexpr (BUF == 0) {
     lds[1][lslot[0]] = aset1[0];
@@ -151,7 +149,7 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
 }
 
 // One work item: 128 rows x (this wavefront's two operand columns), t.nst >= 1 stages.
-template <int MODE, bool GATHER, int BSTRIDE>
+template <int MODE, bool GATHER>
 __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[1024]) {
   constexpr bool GATE_UP = MODE == kModeGateUp;
   const int nst = t.nst;
@@ -181,7 +179,7 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   aset1[1] = *(const u32x4*)(ag[1] + s1);
 #pragma unroll
   for (int q = 0; q < kRing; ++q) {
-    const size_t o = (size_t)min(q, 4 * nst - 1) * BSTRIDE;
+    const size_t o = (size_t)min(q, 4 * nst - 1) * kOperandElems;
     bring[q][0] = *(const u32x4*)(t.b0 + o);
     bring[q][1] = *(const u32x4*)(t.b1 + o);
   }
@@ -190,15 +188,15 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   __syncthreads();
   if (t.rows > 64) {  // block-uniform: a tile with at most 64 live rows skips the others
     for (int s0 = 0; s0 < nst; s0 += 2) {
-      kstage<4, 0, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      kstage<4, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
       if (s0 + 1 < nst)
-        kstage<4, 1, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+        kstage<4, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
   } else {
     for (int s0 = 0; s0 < nst; s0 += 2) {
-      kstage<2, 0, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
+      kstage<2, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
       if (s0 + 1 < nst)
-        kstage<2, 1, BSTRIDE>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+        kstage<2, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
   }
 
@@ -373,18 +371,19 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     t.out = out + (size_t)row0 * Nout + col0;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
-    prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER, kOperandElems>(t, lds_a);
+    prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER>(t, lds_a);
   }
 }
 
 // ------------------------------------------------------------------------------------
 // Weight gradients of every expert (backward pass): out[e][m][n] = sum over the expert's
-// rows k of AT[m][k] BT[n][k], with AT [M][npad] and BT [Ncols][npad] bf16 row-major (the
-// reduction dimension contiguous; each expert's rows padded with zeros to a multiple of
-// 64 starting at poff[e]).  The prefill tile with the roles of the forward: tile rows =
-// 128 of M, a wavefront's two operand columns = 64 of Ncols (512 per block of 8
-// wavefronts), read from BT rows (consecutive k-steps 16 elements apart), K = the rows;
-// fp32 out.  gu_split: Ncols is the interleaved gate|up dimension, the columns go to out
+// rows k of AT[m][k] BT[n][k], with AT [M][npad] bf16 row-major and BT [Ncols][npad] in
+// packed operand order (1 KiB blocks [n / 32][k / 16], like the packed down weights); each
+// expert's rows padded with zeros to a multiple of 64 starting at poff[e].  The prefill
+// tile with the roles of the forward: tile rows = 128 of M, a wavefront's two operand
+// columns = 64 of Ncols (512 per block of 8 wavefronts), each k-step one contiguous 1 KiB
+// operand block, K = the rows; fp32 out.  (With BT row-major, a k-step read 32 B of each of
+// 32 rows per load and every 128-byte line was fetched four times from L2.)  gu_split: Ncols is the interleaved gate|up dimension, the columns go to out
 // (gate) and out2 (up), each [E][M][Ncols / 2].  Grid: (M / 128 rounded up, Ncols / 512
 // rounded up, E); experts without rows get zeros.
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -411,8 +410,8 @@ void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ 
   t.gu_split = gu_split;
   t.A = AT + (size_t)m0 * npad + k0;
   t.rtok = nullptr;
-  t.b0 = BT + (size_t)(nc + (lane & 31)) * npad + k0 + 8 * (lane >> 5);
-  t.b1 = t.b0 + (size_t)32 * npad;
+  t.b0 = BT + ((size_t)(nc >> 5) * (npad >> 4) + (k0 >> 4)) * kOperandElems + lane * 8;
+  t.b1 = t.b0 + (size_t)(npad >> 4) * kOperandElems;  // the next 32 columns
   const size_t orow = (size_t)e * M + m0;
   t.outf = out + orow * (gu_split ? Ncols / 2 : Ncols);
   t.outf2 = gu_split ? out2 + orow * (Ncols / 2) : nullptr;
@@ -420,7 +419,7 @@ void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ 
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane & 31, 2 * kk + (lane >> 5));
   if (t.nst > 0) {  // block-uniform
-    prefill_tile<kModeWgrad, false, 16>(t, lds_a);
+    prefill_tile<kModeWgrad, false>(t, lds_a);
     return;
   }
   if (!t.act) return;

@@ -679,9 +679,9 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
                              p->T <= 24, s);
     if (err == hipSuccess) err = launch_pad_offsets(B.roff, 1, 64, B.rpoff, s);
     if (err == hipSuccess)
-      err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, E, B.tpad, B.dlT, s);
+      err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, E, B.tpad, false, B.dlT, s);
     if (err == hipSuccess)
-      err = launch_transpose_pad(x, nullptr, B.roff, B.rpoff, 1, H, B.tpad, B.xTf, s);
+      err = launch_transpose_pad(x, nullptr, B.roff, B.rpoff, 1, H, B.tpad, true, B.xTf, s);
     if (err == hipSuccess)
       err = launch_wgrad_bf16(B.dlT, B.xTf, B.rpoff, 1, E, H, B.tpad, false, grads->dw_router,
                               nullptr, s);
@@ -693,13 +693,13 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   // weight gradients over each expert's rows
   if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, 64, B.poff, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, H, B.npad, B.xT, s);
+    err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, H, B.npad, false, B.xT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, I, B.npad, B.aT, s);
+    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, I, B.npad, false, B.aT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, H, B.npad, B.dypT, s);
+    err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, H, B.npad, true, B.dypT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, 2 * I, B.npad, B.dguT, s);
+    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, 2 * I, B.npad, true, B.dguT, s);
   if (err == hipSuccess)
     err = launch_wgrad_bf16(B.aT, B.dypT, B.poff, E, I, H, B.npad, false, grads->dw_down,
                             nullptr, s);

@@ -105,9 +105,11 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* 
                               hipStream_t s);
 // [rows, C] bf16 (rows through row_map if not NULL) -> [C, npad], each expert's rows at
 // columns poff[e] .. (a multiple of 64), padding columns zeroed; C % 64 == 0, npad % 64 == 0.
+// packed: dst in matrix-core operand order ([C / 32][npad / 16] blocks of 1 KiB, like the
+// packed down weights with K = npad) instead of row-major.
 hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
-                                const int32_t* poff, int E, int C, int64_t npad, void* dst,
-                                hipStream_t s);
+                                const int32_t* poff, int E, int C, int64_t npad, bool packed,
+                                void* dst, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* in, int64_t n, void* out, hipStream_t s);
 
 // ---- pack.hip
@@ -135,7 +137,9 @@ hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
                             const int32_t* offsets, const void* packed_b, void* out, int K,
                             int Nout, bool decode, hipStream_t s);
 // Weight gradients on the matrix cores: out[e][m][n] = sum_k AT[m][k] BT[n][k] over expert
-// e's rows [poff[e], poff[e + 1]) (a multiple of 64, zero-padded); Ncols % 64 == 0.
+// e's rows [poff[e], poff[e + 1]) (a multiple of 64, zero-padded); Ncols % 64 == 0.  AT is
+// row-major [M][npad]; BT is [Ncols][npad] in the packed operand order of
+// launch_transpose_pad(packed = true).
 hipError_t launch_wgrad_bf16(const void* AT, const void* BT, const int32_t* poff, int E, int M,
                              int Ncols, int64_t npad, bool gu_split, float* out, float* out2,
                              hipStream_t s);
