@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_layer_backward (saved routing and expert outputs of the "
                          "timed forward, bf16 upstream gradient); reported under 'backward'")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="cold-cache pass: a scratch write of this many MiB before every step "
+                         "(0: no cold-cache pass); reported under 'cold_cache'")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
@@ -341,6 +344,29 @@ def main():
     stage_ms = {s: sum(events[i][j].elapsed_time(events[i][j + 1]) for i in range(args.steps)) / args.steps
                 for j, s in enumerate(stages)}
 
+    cold = None
+    if args.flush_mib > 0:
+        # cold-cache pass: a scratch write larger than the 256 MiB last-level cache before
+        # every step, the step timed by events recorded after the write and after the step
+        # (the warm figure timed the same way is the stage pass's first-to-last event)
+        scratch = torch.empty(args.flush_mib << 18, dtype=torch.int32, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            scratch.fill_(1)
+            step(cev[i])
+        torch.cuda.synchronize()
+        del scratch
+        cold_ms = sum(cev[i][0].elapsed_time(cev[i][5]) for i in range(args.steps)) / args.steps
+        warm_ms = sum(events[i][0].elapsed_time(events[i][5]) for i in range(args.steps)) / args.steps
+        cold = {"ms_per_step": round(cold_ms, 4), "tokens_per_s": round(wl.T / cold_ms * 1e3, 1),
+                "warm_ms_per_step_same_timing": round(warm_ms, 4),
+                "stages_us": {s: round(sum(cev[i][j].elapsed_time(cev[i][j + 1])
+                                           for i in range(args.steps)) / args.steps * 1e3, 2)
+                              for j, s in enumerate(stages)},
+                "flush_bytes": args.flush_mib << 20,
+                "how": "each step after a scratch write of flush_bytes, timed by events between "
+                       "the stages (as the stage pass)"}
+
     N = int(disp["offsets"][-1].item())
     E_hit = int((disp["counts"] > 0).sum().item())
     alg = algorithmic(wl, N, E_hit, router=args.router)
@@ -366,6 +392,8 @@ def main():
                    "capacity": wl.capacity, "N_kept": N, "experts_hit": E_hit},
         "roofline": roof, "stages": per_stage,
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     if layer_calls is not None:
         out["layer_calls"] = layer_calls
     if backward is not None:
