@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -104,10 +105,16 @@ def roofline_of(stage, alg, sec, dtype):
                 frac=round(ach / PEAK_HBM_GBS, 4))
 
 
-def kernel_source_hash():
+def kernel_source_hash(csrc=None):
+    """Hash of the kernel sources with comments and blank lines removed (a comment edit
+    leaves the kernels, and so the recorded counters, valid)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "expert_ffn_moe_amd", "csrc"))):
-        h.update(open(os.path.join(ROOT, "expert_ffn_moe_amd", "csrc", f), "rb").read())
+    csrc = csrc or os.path.join(ROOT, "expert_ffn_moe_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        text = open(os.path.join(csrc, f), encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
+        h.update(f.encode() + b"\0" + "\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

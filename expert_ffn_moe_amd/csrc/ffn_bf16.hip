@@ -9,10 +9,11 @@
 //
 // Two kernel shapes, chosen from the problem shape:
 //  * prefill (many rows per expert): persistent, XCD-aware grouped GEMM over 128-row M
-//    tiles; the activation tile goes through LDS (shared by the 4 wavefronts of a block)
+//    tiles; the activation tile goes through LDS (shared by the 8 wavefronts of a block)
 //    and each wavefront streams its own weight operands straight into registers in
 //    matrix-core operand order (the packed layout makes each operand a contiguous 1 KiB).
-//    v_mfma_f32_32x32x16_bf16.
+//    v_mfma_f32_32x32x16_bf16.  The same tile computes the backward pass's weight
+//    gradients (wgrad_kernel).
 //  * decode (a few rows per expert): a weight-streaming kernel; one wavefront per
 //    32/64-column panel of one expert, 16-row M steps, v_mfma_f32_16x16x32_bf16.
 #include <algorithm>

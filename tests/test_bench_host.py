@@ -74,3 +74,13 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_kernel_source_hash_ignores_comments_only(tmp_path):
+    src = tmp_path / "k.hip"
+    src.write_text("__global__ void k(int* p) {\n  p[0] = 1;\n}\n")
+    h0 = bench.kernel_source_hash(str(tmp_path))
+    src.write_text("// a kernel\n__global__ void k(int* p) {  /* one store */\n\n  p[0] = 1;  // x\n}\n")
+    assert bench.kernel_source_hash(str(tmp_path)) == h0
+    src.write_text("__global__ void k(int* p) {\n  p[0] = 2;\n}\n")
+    assert bench.kernel_source_hash(str(tmp_path)) != h0
