@@ -116,6 +116,10 @@ ROUTER = [
     ("e128", 513, 512, 128, 8, 1, 1, 0),
     ("e256_grouped", 300, 1024, 256, 8, 8, 4, 0),
     ("e64_cap", 2000, 256, 64, 4, 1, 1, 100),
+    # multiples of 32 that are not of 64: staged gate pieces not a multiple of the threads
+    ("e32", 70, 64, 32, 4, 1, 1, 0),
+    ("e96", 333, 192, 96, 6, 3, 2, 0),
+    ("e224_grouped", 1000, 128, 224, 8, 8, 4, 0),
 ]
 
 
