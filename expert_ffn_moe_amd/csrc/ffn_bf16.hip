@@ -188,17 +188,22 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   lds[0][lslot[1]] = aset0[1];
   __syncthreads();
   if (t.rows > 64) {  // block-uniform: a tile with at most 64 live rows skips the others
-    for (int s0 = 0; s0 < nst; s0 += 2) {
+    // stages in pairs with an odd last stage peeled off: with the second stage of a pair
+    // conditional, the compiler sank the first stage's activation loads into it (their
+    // only use), leaving them one stage of latency instead of two
+    int s0 = 0;
+    for (; s0 + 1 < nst; s0 += 2) {
       kstage<4, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
-      if (s0 + 1 < nst)
-        kstage<4, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+      kstage<4, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
+    if (s0 < nst) kstage<4, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
   } else {
-    for (int s0 = 0; s0 < nst; s0 += 2) {
+    int s0 = 0;
+    for (; s0 + 1 < nst; s0 += 2) {
       kstage<2, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
-      if (s0 + 1 < nst)
-        kstage<2, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
+      kstage<2, 1>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0 + 1, nst);
     }
+    if (s0 < nst) kstage<2, 0>(acc, bring, aset0, aset1, lds, ag, lslot, t, s0, nst);
   }
 
   if constexpr (MODE == kModeWgrad) {
