@@ -374,9 +374,39 @@ def main():
                 "how": "each step after a scratch write of flush_bytes, timed by events between "
                        "the stages (as the stage pass)"}
 
+    # the dispatch with the row copy (moe_dispatch with xp: the layout, then the token rows
+    # gathered into expert order), timed on its own: the layer step folds the gather into
+    # the gate/up GEMM's activation loads instead
+    xp = torch.empty(tk, wl.H, dtype=dt, device=dev)
+    drows = dict(disp, xp=xp)
+    keep_in = routing[2] if wl.capacity > 0 else None
+    for _ in range(3):
+        moe.dispatch(p, inp["x"], routing[0], keep_in, out=drows, ws=ws[moe.OP_DISPATCH], rows=True)
+    dev_ = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        dev_[i][0].record()
+        moe.dispatch(p, inp["x"], routing[0], keep_in, out=drows, ws=ws[moe.OP_DISPATCH], rows=True)
+        dev_[i][1].record()
+    torch.cuda.synchronize()
+    drows_ms = sum(e[0].elapsed_time(e[1]) for e in dev_) / args.steps
+    del xp, drows
+
     N = int(disp["offsets"][-1].item())
     E_hit = int((disp["counts"] > 0).sum().item())
     alg = algorithmic(wl, N, E_hit, router=args.router)
+    b_act = 4 if wl.dtype == "f32" else 2
+    row_bytes = wl.T * wl.H * b_act + N * wl.H * b_act  # x rows in, their k copies out
+    copy_ms = max(drows_ms - stage_ms["dispatch"], 1e-6)
+    dispatch_rows = {
+        "us": round(drows_ms * 1e3, 2), "bound": "hbm",
+        "achieved": round((alg["dispatch"]["bytes"] + row_bytes) / (drows_ms * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "frac": round((alg["dispatch"]["bytes"] + row_bytes) / (drows_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "row_copy_us": round(copy_ms * 1e3, 2),
+        "row_copy_frac": round(row_bytes / (copy_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "how": "moe_dispatch with xp timed alone; the row copy is that time less the layout-only "
+               "dispatch stage",
+    }
     dom = max(("gate_up", "down", "dispatch", "combine", "route"), key=lambda s: stage_ms[s])
     roof = roofline_of(dom, alg, stage_ms[dom] / 1e3, wl.dtype)
     roof["kernel"] = dom
@@ -399,6 +429,7 @@ def main():
                    "capacity": wl.capacity, "N_kept": N, "experts_hit": E_hit},
         "roofline": roof, "stages": per_stage,
     }
+    out["dispatch_rows"] = dispatch_rows
     if cold is not None:
         out["cold_cache"] = cold
     if layer_calls is not None:

@@ -219,10 +219,13 @@ __global__ __launch_bounds__(kCapThreads) void capacity_select_kernel(
     if (key_at(i) < prefix) keep[slots[i]] = 0;
 }
 
-// One token per block: read x[t] once, write it to each of its rows.
-__global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x,
-                                                     const int32_t* __restrict__ slot_to_row,
-                                                     int k, int nvec, uint4* __restrict__ xp) {
+// One token per block: read x[t] once, write it to each of its rows.  NT: the row copies
+// are stored with the non-temporal hint (written once, read later by another kernel).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool NT>
+__global__ __launch_bounds__(1024) void gather_kernel(const uint4* __restrict__ x,
+                                                      const int32_t* __restrict__ slot_to_row,
+                                                      int k, int nvec, uint4* __restrict__ xp) {
   __shared__ int rows[32];
   const int t = blockIdx.x;
   if (threadIdx.x < k) rows[threadIdx.x] = slot_to_row[(size_t)t * k + threadIdx.x];
@@ -231,7 +234,12 @@ __global__ __launch_bounds__(256) void gather_kernel(const uint4* __restrict__ x
     const uint4 d = x[(size_t)t * nvec + v];
     for (int j = 0; j < k; ++j) {
       const int r = rows[j];
-      if (r >= 0) xp[(size_t)r * nvec + v] = d;
+      if (r < 0) continue;
+      if constexpr (NT)
+        __builtin_nontemporal_store(u32x4_t{d.x, d.y, d.z, d.w},
+                                    reinterpret_cast<u32x4_t*>(&xp[(size_t)r * nvec + v]));
+      else
+        xp[(size_t)r * nvec + v] = d;
     }
   }
 }
@@ -296,8 +304,16 @@ hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slo
                          void* xp, hipStream_t s) {
   const size_t row_bytes = (size_t)p.H * (p.act_dtype == MOE_BF16 ? 2 : 4);
   const int nvec = (int)(row_bytes / 16);
-  hipLaunchKernelGGL(gather_kernel, dim3(p.T), dim3(256), 0, s, (const uint4*)x, slot_to_row,
-                     p.k, nvec, (uint4*)xp);
+  // one thread per 16-byte vector of a row when a row has at most 1024 of them; past 256 MiB
+  // of xp (the size of the last-level cache) the copies are streamed with the
+  // non-temporal hint, as in the combine
+  const int threads = nvec <= 1024 ? (nvec + 63) / 64 * 64 : 256;
+  if ((int64_t)p.T * p.k * (int64_t)row_bytes > ((int64_t)256 << 20))
+    hipLaunchKernelGGL(gather_kernel<true>, dim3(p.T), dim3(threads), 0, s, (const uint4*)x,
+                       slot_to_row, p.k, nvec, (uint4*)xp);
+  else
+    hipLaunchKernelGGL(gather_kernel<false>, dim3(p.T), dim3(threads), 0, s, (const uint4*)x,
+                       slot_to_row, p.k, nvec, (uint4*)xp);
   return hipGetLastError();
 }
 
