@@ -41,7 +41,7 @@ __global__ __launch_bounds__(1024) void combine_bf16_kernel(const uint4* __restr
   __shared__ int rows[32];
   __shared__ float wt[32];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = s2r[(size_t)t * k + threadIdx.x];
     wt[threadIdx.x] = w ? w[(size_t)t * k + threadIdx.x] : 1.0f;  // NULL: unit weights
   }
@@ -93,7 +93,7 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float4* __restri
   __shared__ int rows[32];
   __shared__ float wt[32];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) {
+  if ((int)threadIdx.x < k) {
     rows[threadIdx.x] = s2r[(size_t)t * k + threadIdx.x];
     wt[threadIdx.x] = w ? w[(size_t)t * k + threadIdx.x] : 1.0f;  // NULL: unit weights
   }

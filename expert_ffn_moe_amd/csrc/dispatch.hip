@@ -228,7 +228,7 @@ __global__ __launch_bounds__(1024) void gather_kernel(const uint4* __restrict__ 
                                                       int k, int nvec, uint4* __restrict__ xp) {
   __shared__ int rows[32];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) rows[threadIdx.x] = slot_to_row[(size_t)t * k + threadIdx.x];
+  if ((int)threadIdx.x < k) rows[threadIdx.x] = slot_to_row[(size_t)t * k + threadIdx.x];
   __syncthreads();
   for (int v = threadIdx.x; v < nvec; v += blockDim.x) {
     const uint4 d = x[(size_t)t * nvec + v];

@@ -480,7 +480,6 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
     const int ar = row_beg + min(m0 + (lane & 15), cnt - 1);
     const size_t src_row = GATHER ? (size_t)row_token[ar] : (size_t)ar;
     const uint16_t* ap = A + src_row * K + 8 * (lane >> 4);
-#pragma unroll 4
     for (int ks = 0; ks < nks; ++ks) {
       const uint4 av = *(const uint4*)(ap + ks * 32);
       const size_t o = (size_t)(2 * ks + ksub) * kOperandElems + lofs;
