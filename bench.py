@@ -40,8 +40,10 @@ PROFILES = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU reaches its steady clock only after some 50-100 ms of back-to-back steps (a
+    # 0.46 ms step runs at ~0.50 ms over the first 20): the defaults warm up for 200 steps
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--router", action="store_true",
                     help="route from the hidden states: router GEMM x W_r^T + selection "
