@@ -31,6 +31,9 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // One token per block: dyp rows of its kept slots and the gradient of its routing weights.
+// The slots are independent (no barrier between them, so the loads of several slots can be
+// in flight together); each wavefront leaves its partial dot product per slot in LDS and one
+// barrier at the end precedes the per-slot sums.
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dy,
                                                           const uint4* __restrict__ yp,
                                                           const float* __restrict__ w,
@@ -38,49 +41,43 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                                           int k, int nvec,
                                                           uint4* __restrict__ dyp,
                                                           float* __restrict__ dw) {
-  __shared__ int rows[32];
-  __shared__ float wt[32];
-  __shared__ float red[4];
+  __shared__ float red[32][4];
   const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < k) {
-    rows[tid] = s2r[(size_t)t * k + tid];
-    wt[tid] = w[(size_t)t * k + tid];
-  }
   float f[4][8];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int v = tid + 256 * q;
     if (v < nvec) unpack8(dy[(size_t)t * nvec + v], f[q]);
   }
-  __syncthreads();
+#pragma unroll 4
   for (int j = 0; j < k; ++j) {
-    const int r = rows[j];  // block-uniform
-    if (r < 0) {
-      if (tid == 0) dw[(size_t)t * k + j] = 0.0f;
-      continue;
-    }
-    const float wj = wt[j];
+    const int r = s2r[(size_t)t * k + j];  // block-uniform
+    const float wj = w[(size_t)t * k + j];
     float dot = 0.0f;
+    if (r >= 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int v = tid + 256 * q;
-      if (v < nvec) {
-        float y8[8], o[8];
-        unpack8(yp[(size_t)r * nvec + v], y8);
+      for (int q = 0; q < 4; ++q) {
+        const int v = tid + 256 * q;
+        if (v < nvec) {
+          float y8[8], o[8];
+          unpack8(yp[(size_t)r * nvec + v], y8);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          o[i] = wj * f[q][i];
-          dot = __builtin_fmaf(y8[i], f[q][i], dot);
+          for (int i = 0; i < 8; ++i) {
+            o[i] = wj * f[q][i];
+            dot = __builtin_fmaf(y8[i], f[q][i], dot);
+          }
+          dyp[(size_t)r * nvec + v] = pack8(o);
         }
-        dyp[(size_t)r * nvec + v] = pack8(o);
       }
     }
     dot = wave_sum(dot);
-    if ((tid & 63) == 0) red[tid >> 6] = dot;
-    __syncthreads();
-    if (tid == 0) dw[(size_t)t * k + j] = (red[0] + red[1]) + (red[2] + red[3]);
-    __syncthreads();
+    if ((tid & 63) == 0) red[j][tid >> 6] = dot;
   }
+  __syncthreads();
+  if (tid < k)
+    dw[(size_t)t * k + tid] = s2r[(size_t)t * k + tid] < 0
+                                  ? 0.0f
+                                  : (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
 // SwiGLU backward on the interleaved gate|up rows (32-column blocks of g and u alternate),
@@ -138,11 +135,15 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
 
 // dst[c][q] for the padded columns q of a block: column q = poff[e] + i holds src row
 // offsets[e] + i (through row_map if given) while i < count_e, zeros after.  A block takes
-// 64 destination columns x 64 values of c: loads 64 source rows (128 contiguous bytes
-// each), stores 64 destination rows (128 contiguous bytes each) through LDS.
+// 64 destination columns x up to kTransposeChunks chunks of 64 values of c: it finds the
+// source rows once, loads every chunk (128 contiguous bytes of each source row per chunk,
+// all in flight together), then per chunk stores 64 destination rows (128 contiguous bytes
+// each) through LDS.
 // PACKED: dst in matrix-core operand order instead (the weight-gradient GEMM's B operand):
 // 1 KiB blocks of 32 values of c x 16 columns q, ordered [c / 32][q / 16]; piece
 // (c % 32) + 32 h of a block holds columns 8 h .. + 7 of value c.
+constexpr int kTransposeChunks = 4;
+
 template <bool PACKED>
 __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
                                                             const int32_t* __restrict__ row_map,
@@ -152,7 +153,8 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ dst) {
   __shared__ uint32_t tile[64][33];  // [destination column][pairs of c], padded row
   __shared__ int srow[64];
-  const int q0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const int q0 = blockIdx.x * 64, cb = blockIdx.y * 64 * kTransposeChunks;
+  const int nch = min(kTransposeChunks, (C - cb) / 64);
   if (q0 >= poff[E]) return;  // block-uniform
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -166,22 +168,33 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
     srow[tid] = r < offsets[lo + 1] ? (row_map ? row_map[r] : r) : -1;
   }
   __syncthreads();
+  const int j = tid >> 2, part = tid & 3;  // load: column j, values 16 part .. + 15 of a chunk
+  uint4 v[kTransposeChunks][2];
   {
-    const int j = tid >> 2, part = tid & 3;  // column j, values 16 part .. + 15
     const int r = srow[j];
-    uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-    if (r >= 0) {
-      const uint4* p = reinterpret_cast<const uint4*>(src + (int64_t)r * C + c0 + 16 * part);
-      v0 = p[0];
-      v1 = p[1];
+#pragma unroll
+    for (int ch = 0; ch < kTransposeChunks; ++ch) {
+      v[ch][0] = v[ch][1] = make_uint4(0, 0, 0, 0);
+      if (r >= 0 && ch < nch) {
+        const uint4* p =
+            reinterpret_cast<const uint4*>(src + (int64_t)r * C + cb + 64 * ch + 16 * part);
+        v[ch][0] = p[0];
+        v[ch][1] = p[1];
+      }
     }
-    uint32_t* t = &tile[j][8 * part];
-    t[0] = v0.x; t[1] = v0.y; t[2] = v0.z; t[3] = v0.w;
-    t[4] = v1.x; t[5] = v1.y; t[6] = v1.z; t[7] = v1.w;
   }
-  __syncthreads();
-  {
-    const int cc = tid >> 2, part = tid & 3;  // value c0 + cc, columns 16 part .. + 15
+#pragma unroll
+  for (int ch = 0; ch < kTransposeChunks; ++ch) {
+    if (ch >= nch) break;  // block-uniform
+    if (ch > 0) __syncthreads();  // the previous chunk's reads of the tile are done
+    {
+      uint32_t* t = &tile[j][8 * part];
+      t[0] = v[ch][0].x; t[1] = v[ch][0].y; t[2] = v[ch][0].z; t[3] = v[ch][0].w;
+      t[4] = v[ch][1].x; t[5] = v[ch][1].y; t[6] = v[ch][1].z; t[7] = v[ch][1].w;
+    }
+    __syncthreads();
+    const int c0 = cb + 64 * ch;
+    const int cc = tid >> 2;  // store: value c0 + cc, columns 16 part .. + 15
     uint32_t w[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -242,7 +255,7 @@ hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* 
 hipError_t launch_transpose_pad(const void* src, const int32_t* row_map, const int32_t* offsets,
                                 const int32_t* poff, int E, int C, int64_t npad, bool packed,
                                 void* dst, hipStream_t s) {
-  const dim3 grid((unsigned)(npad / 64), (unsigned)(C / 64));
+  const dim3 grid((unsigned)(npad / 64), (unsigned)div_up(C / 64, kTransposeChunks));
   if (packed)
     hipLaunchKernelGGL(transpose_pad_kernel<true>, grid, dim3(256), 0, s, (const uint16_t*)src,
                        row_map, offsets, poff, E, C, npad, (uint16_t*)dst);

@@ -207,27 +207,43 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
   }
 
   if constexpr (MODE == kModeWgrad) {
-    // fp32 straight from the accumulators: for each register, the 32 lanes of a half
-    // wavefront write 32 consecutive floats of one row
+    // fp32 through LDS: per (32-row fragment, operand column) the wavefront writes its
+    // 32 x 32 block row-major into its own 4 KiB of LDS (a half wavefront writes one row
+    // of 32 consecutive floats per register) and stores it in 16-byte pieces, 8 lanes per
+    // 128-byte row piece, with the non-temporal hint (the gradients are written once and
+    // are far larger than the caches).  The region is the wavefront's own and a
+    // wavefront's LDS accesses complete in order, so the phases need only a compiler
+    // barrier.
     if (!t.act) return;
-    const int col = t.col0 + (lane & 31);
+    float* const ldsf = reinterpret_cast<float*>(&lds[0][0]) + wave * 1024;
+    const int wofs = (lane >> 5) * 4 * 32 + (lane & 31);
+    const int qrow = lane >> 3, qcol = (lane & 7) * 4;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 4; ++m) {
+      if (m * 32 >= t.rows) break;  // block-uniform
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = m * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (r >= t.rows) continue;
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int n = col + 32 * h;
-          if (!t.gu_split) {
-            t.outf[(size_t)r * t.Nout + n] = acc[m][h][i];
-          } else {  // interleaved gate|up columns: 64 b + j -> gate (j < 32) or up column 32 b + j % 32
-            float* o = (n & 32) ? t.outf2 : t.outf;
-            o[(size_t)r * (t.Nout / 2) + 32 * (n >> 6) + (n & 31)] = acc[m][h][i];
-          }
+        for (int i = 0; i < 16; ++i) ldsf[wofs + ((i >> 2) * 8 + (i & 3)) * 32] = acc[m][h][i];
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        float* o;
+        size_t ld;
+        if (!t.gu_split) {
+          o = t.outf + t.col0 + 32 * h;
+          ld = t.Nout;
+        } else {  // interleaved gate|up columns: operand column 0 -> gate, 1 -> up
+          o = (h ? t.outf2 : t.outf) + 32 * (t.col0 >> 6);
+          ld = t.Nout / 2;
         }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const int rr = qrow + 8 * p, r = m * 32 + rr;
+          const f32x4_t v = *(const f32x4_t*)(ldsf + rr * 32 + qcol);
+          if (r < t.rows) __builtin_nontemporal_store(v, (f32x4_t*)(o + (size_t)r * ld + qcol));
+        }
+        __asm__ volatile("" ::: "memory");
       }
+    }
     return;
   }
 
