@@ -115,6 +115,10 @@ SMALL = [
              logits="normal+bias0.5", seed=73),
     Workload("bwd_one_expert", T=70, H=128, E=1, k=1, I=64, capacity=0, dtype="bf16",
              logits="normal", seed=74),
+    # several 128-row gradient tiles (the last of 64 rows), column groups with idle
+    # wavefronts, skewed experts with odd stage counts along their rows
+    Workload("bwd_multi_tile", T=1000, H=384, E=8, k=2, I=320, capacity=0, dtype="bf16",
+             logits="normal+zipf1.2", seed=76),
 ]
 
 
