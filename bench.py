@@ -55,7 +55,7 @@ def parse():
     ap.add_argument("--shared-I", type=int, default=0,
                     help="with --chunk-tokens: a shared expert of this intermediate width")
     ap.add_argument("--backward", action="store_true",
-                    help="also time moe_layer_backward (saved routing and expert outputs of the "
+                    help="also time moe_layer_backward (saved routing, expert outputs and g|u of the "
                          "timed forward, bf16 upstream gradient); reported under 'backward'")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="cold-cache pass: a scratch write of this many MiB before every step "
@@ -237,8 +237,11 @@ def time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev):
 
 def time_backward(args, moe, p, wl, inp, pgu, pd, routing, disp, yp, dev):
     """ms per moe_layer_backward call on the last forward's routing and expert outputs, and
-    the matrix-core rate over its GEMM flops (data gradients: da 2NHI, g|u recompute 4NHI,
-    dxp 4NHI; weight gradients 2NHI + 4NHI)."""
+    the matrix-core rate over its GEMM flops (data gradients: da 2NHI, dxp 4NHI; weight
+    gradients 2NHI + 4NHI; the g|u recompute 4NHI more when the forward did not save them).
+    Timed twice: with the pre-activations saved by the forward's gate/up
+    (moe_expert_gate_up_gather_gu), and recomputing them; plus what saving them adds to the
+    forward's gate/up."""
     import torch
 
     if wl.dtype != "bf16":
@@ -250,21 +253,38 @@ def time_backward(args, moe, p, wl, inp, pgu, pd, routing, disp, yp, dev):
     saved = dict(topk_ids=routing[0], topk_w=routing[1], offsets=disp["offsets"],
                  row_token=disp["row_token"], slot_to_row=disp["slot_to_row"])
     ws = moe.workspace(p, moe.OP_BACKWARD, dev)
-    fn = lambda: moe.layer_backward(p, inp["x"], inp["logits"], pgu, pd, pbgu, pbd, saved, dy,
-                                    yp=yp, ws=ws)
-    for _ in range(max(2, args.warmup // 4)):
-        fn()
-    torch.cuda.synchronize()
+    a_buf, gu = moe.expert_gate_up_gather_gu(p, inp["x"], disp["row_token"], disp["offsets"], pgu)
+
+    def timed(fn, n):
+        for _ in range(max(2, args.warmup // 4)):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / n
+
     n = max(3, args.steps // 2)
-    t0 = time.perf_counter()
-    for _ in range(n):
-        fn()
-    torch.cuda.synchronize()
-    sec = (time.perf_counter() - t0) / n
+    common = (p, inp["x"], inp["logits"], pgu, pd, pbgu, pbd, saved, dy)
+    sec = timed(lambda: moe.layer_backward(*common, yp=yp, ws=ws, gu=gu), n)
+    sec_rc = timed(lambda: moe.layer_backward(*common, yp=yp, ws=ws), n)
+    m = max(5, args.steps)
+    gu_fwd = timed(lambda: moe.expert_gate_up_gather_gu(p, inp["x"], disp["row_token"],
+                                                        disp["offsets"], pgu, out=a_buf, gu=gu), m)
+    plain_fwd = timed(lambda: moe.expert_gate_up_gather(p, inp["x"], disp["row_token"],
+                                                        disp["offsets"], pgu, out=a_buf), m)
     N = int(disp["offsets"][-1].item())
-    flops = 16 * N * wl.H * wl.I
-    return {"ms": round(sec * 1e3, 4), "calls": n, "gemm_tflops": round(flops / sec / 1e12, 1),
-            "frac_bf16_peak": round(flops / sec / 1e12 / PEAK_TFLOPS["bf16"], 4),
+    flops = 12 * N * wl.H * wl.I
+    flops_rc = 16 * N * wl.H * wl.I
+    peak = PEAK_TFLOPS["bf16"]
+    return {"ms": round(sec * 1e3, 4), "calls": n, "with": "the forward's saved g|u",
+            "gemm_tflops": round(flops / sec / 1e12, 1),
+            "frac_bf16_peak": round(flops / sec / 1e12 / peak, 4),
+            "ms_recompute_gu": round(sec_rc * 1e3, 4),
+            "frac_bf16_peak_recompute_gu": round(flops_rc / sec_rc / 1e12 / peak, 4),
+            "forward_gate_up_us": {"plain": round(plain_fwd * 1e6, 1),
+                                   "saving_gu": round(gu_fwd * 1e6, 1)},
             "workspace_bytes": int(ws.numel())}
 
 

@@ -37,7 +37,8 @@ EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_pa
            "moe_expert_gate_up_gather",
            "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
            "moe_route_grouped", "moe_router", "moe_layer_chunked_workspace_bytes",
-           "moe_layer_chunked", "moe_pack_weights_backward", "moe_layer_backward")
+           "moe_layer_chunked", "moe_pack_weights_backward", "moe_expert_gate_up_gather_gu",
+           "moe_layer_backward")
 
 
 class MoeError(RuntimeError):
@@ -95,8 +96,9 @@ def _load() -> ctypes.CDLL:
                                       sz, P]),
         "moe_layer_chunked_workspace_bytes": (sz, [PP, ctypes.c_int32, ctypes.c_int32]),
         "moe_pack_weights_backward": (ctypes.c_int, [PP, P, P, P, P, P, P]),
+        "moe_expert_gate_up_gather_gu": (ctypes.c_int, [PP, P, P, P, P, P, P, P]),
         "moe_layer_backward": (ctypes.c_int, [PP, P, P, P, P, P, P, P,
-                                              ctypes.POINTER(MoeSavedRouting), P, P,
+                                              ctypes.POINTER(MoeSavedRouting), P, P, P,
                                               ctypes.POINTER(MoeGrads), P, sz, P]),
         "moe_layer_chunked": (ctypes.c_int, [PP, P, P, P, P, ctypes.POINTER(MoeSharedExpert),
                                              ctypes.c_int32, P, P, sz, P, P]),
@@ -458,16 +460,37 @@ def pack_weights_backward(p: Problem, w_gate, w_up, w_down):
     return pgu, pd
 
 
+def expert_gate_up_gather_gu(p: Problem, x, row_token, offsets, packed_gate_up, out=None,
+                             gu=None):
+    """expert_gate_up_gather (bf16) that also stores the pre-activations g|u for the
+    backward; returns (a [T*k, I], gu [T*k, 2I])."""
+    tk = p.T * p.k
+    _need(x, "x", (p.T, p.H), torch.bfloat16)
+    _need(row_token, "row_token", (tk,), torch.int32)
+    _need(offsets, "offsets", (p.E + 1,), torch.int32)
+    a = _empty((tk, p.I), torch.bfloat16, x.device) if out is None else out
+    _need(a, "a", (tk, p.I), torch.bfloat16)
+    gu = _empty((tk, 2 * p.I), torch.bfloat16, x.device) if gu is None else gu
+    _need(gu, "gu", (tk, 2 * p.I), torch.bfloat16)
+    c = p.c()
+    _call("moe_expert_gate_up_gather_gu", ctypes.byref(c), _ptr(x), _ptr(row_token),
+          _ptr(offsets), _ptr(packed_gate_up), _ptr(a), _ptr(gu), _stream())
+    return a, gu
+
+
 def layer_backward(p: Problem, x, logits, packed_gate_up, packed_down, packed_bwd_gate_up,
-                   packed_bwd_down, routing, dy, yp=None, w_router=None, ws=None):
+                   packed_bwd_down, routing, dy, yp=None, w_router=None, ws=None, gu=None):
     """Gradients of the layer (see moe_layer_backward).  routing: the forward's topk_ids,
     topk_w, offsets, row_token, slot_to_row (a dict); yp: the forward's expert outputs or
-    None (recomputed).  Returns dict(dx, dw_gate, dw_up, dw_down, dlogits, dtopk_w[,
+    None (recomputed); gu: the forward's pre-activations (expert_gate_up_gather_gu) or None
+    (recomputed).  Returns dict(dx, dw_gate, dw_up, dw_down, dlogits, dtopk_w[,
     dw_router])."""
     _need(x, "x", (p.T, p.H), torch.bfloat16)
     _need(dy, "dy", (p.T, p.H), torch.bfloat16)
     if yp is not None:
         _need(yp, "yp", (p.T * p.k, p.H), torch.bfloat16)
+    if gu is not None:
+        _need(gu, "gu", (p.T * p.k, 2 * p.I), torch.bfloat16)
     dev = x.device
     f32 = torch.float32
     g = dict(dx=_empty((p.T, p.H), torch.bfloat16, dev),
@@ -485,7 +508,8 @@ def layer_backward(p: Problem, x, logits, packed_gate_up, packed_down, packed_bw
     c = p.c()
     _call("moe_layer_backward", ctypes.byref(c), _ptr(x), _ptr(logits), _ptr(w_router),
           _ptr(packed_gate_up), _ptr(packed_down), _ptr(packed_bwd_gate_up), _ptr(packed_bwd_down),
-          ctypes.byref(sv), _ptr(yp), _ptr(dy), ctypes.byref(gr), _ptr(ws), ws.numel(), _stream())
+          ctypes.byref(sv), _ptr(yp), _ptr(gu), _ptr(dy), ctypes.byref(gr), _ptr(ws), ws.numel(),
+          _stream())
     return g
 
 

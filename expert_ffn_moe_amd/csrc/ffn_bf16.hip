@@ -55,6 +55,7 @@ struct TileArgs {
   const uint16_t* b0;    // this wavefront's first operand column (lane offset applied)
   const uint16_t* b1;    // second operand column
   uint16_t* out;         // output row row0, column col0 (row stride Nout)
+  uint16_t* out2;        // gate/up saving g|u: that row of gu, column 2 col0 (row stride 2 Nout)
   float* outf;           // weight gradients: fp32 output row row0, column col0
   float* outf2;          // ... its up half when the columns are the interleaved gate|up
   int K, Nout, rows, wave, lane, act;
@@ -150,7 +151,7 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[4][2], u32x4 (&bring)[kRi
 }
 
 // One work item: 128 rows x (this wavefront's two operand columns), t.nst >= 1 stages.
-template <int MODE, bool GATHER>
+template <int MODE, bool GATHER, bool SAVE_GU = false>
 __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[1024]) {
   constexpr bool GATE_UP = MODE == kModeGateUp;
   const int nst = t.nst;
@@ -260,6 +261,28 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     if (m * 32 < t.rows) {  // block-uniform
+      if constexpr (GATE_UP && SAVE_GU) {
+        // the pre-activations first, as the plain GEMM over the same operand columns stores
+        // them: a 32 x 64 block, the gate column's 32 values then the up column's
+        const int wofs2 = (lane >> 5) * 4 * 64 + (lane & 31);
+        const int qrow2 = lane >> 3, qcol2 = (lane & 7) * 8;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          uint16_t* srow = lds16 + wofs2 + ((i >> 2) * 8 + (i & 3)) * 64;
+          srow[0] = to_bf16(acc[m][0][i]);
+          srow[32] = to_bf16(acc[m][1][i]);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q0 = 0; q0 < 256; q0 += 64) {
+          const int rr = qrow2 + q0 / 8;
+          const int r = m * 32 + rr;
+          if (t.act && r < t.rows)
+            *(u32x4*)(t.out2 + (size_t)r * 2 * t.Nout + qcol2) =
+                *(const u32x4*)(lds16 + rr * 64 + qcol2);
+        }
+        __syncthreads();
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         uint16_t* srow = lds16 + wofs + ((i >> 2) * 8 + (i & 3)) * ncol;
@@ -305,11 +328,14 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
 // ------------------------------------------------------------------------------------
 // GATHER (gate/up only): the activation rows are token rows x[row_token[r]] instead of
 // xp[r], so the dispatch row copy is folded into this kernel's activation loads.
-template <bool GATE_UP, bool GATHER>
+// SAVE_GU (gate/up only): the pre-activations g|u are stored too, into gu [rows, 2 Nout] in
+// the layout (and with the bits) of the plain GEMM over the packed gate/up weights.
+template <bool GATE_UP, bool GATHER, bool SAVE_GU = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
                     const int32_t* __restrict__ offsets, int E,
-                    const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout) {
+                    const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout,
+                    uint16_t* __restrict__ gu) {
   __shared__ u32x4 lds_a[2][1024];  // two activation stages (see a_slot)
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_wsum[kWaves];
@@ -391,9 +417,10 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
     t.A = GATHER ? A : A + (size_t)row0 * K;
     t.rtok = GATHER ? row_token + row0 : nullptr;
     t.out = out + (size_t)row0 * Nout + col0;
+    t.out2 = SAVE_GU ? gu + (size_t)row0 * 2 * Nout + 2 * col0 : nullptr;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
-    prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER>(t, lds_a);
+    prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER, SAVE_GU>(t, lds_a);
   }
 }
 
@@ -438,6 +465,7 @@ void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ 
   t.outf = out + orow * (gu_split ? Ncols / 2 : Ncols);
   t.outf2 = gu_split ? out2 + orow * (Ncols / 2) : nullptr;
   t.out = nullptr;
+  t.out2 = nullptr;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane & 31, 2 * kk + (lane >> 5));
   if (t.nst > 0) {  // block-uniform
@@ -461,13 +489,14 @@ void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ 
 //   GATE_UP: 32 columns of `a` (gate + up operand columns); DOWN: 64 columns of yp.
 // Each k-step of 32 issues 4 B operand loads (16 columns each) and one A load.
 // ------------------------------------------------------------------------------------
-template <bool GATE_UP, bool GATHER>
+template <bool GATE_UP, bool GATHER, bool SAVE_GU = false>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A,
                                                      const int32_t* __restrict__ row_token,
                                                      const int32_t* __restrict__ offsets,
                                                      const uint16_t* __restrict__ Bp,
                                                      uint16_t* __restrict__ out, int K,
-                                                     int Nout) {
+                                                     int Nout,
+                                                     uint16_t* __restrict__ gu) {
   const int e = blockIdx.y;
   const int row_beg = offsets[e];
   const int cnt = offsets[e + 1] - row_beg;
@@ -521,6 +550,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
         const int c = g * 32 + (lane & 15);
         o[c] = to_bf16(silu_mul(acc[0][i], acc[2][i]));
         o[c + 16] = to_bf16(silu_mul(acc[1][i], acc[3][i]));
+        if constexpr (SAVE_GU) {  // g|u as the plain GEMM stores them (columns 64 g ..)
+          uint16_t* o2 = gu + (size_t)(row_beg + r) * 2 * Nout + g * 64 + (lane & 15);
+          o2[0] = to_bf16(acc[0][i]);
+          o2[16] = to_bf16(acc[1][i]);
+          o2[32] = to_bf16(acc[2][i]);
+          o2[48] = to_bf16(acc[3][i]);
+        }
       } else {
         const int c = g * 64 + (lane & 15);
         o[c] = to_bf16(acc[0][i]);
@@ -563,30 +599,34 @@ int persistent_grid() { return std::max(kXcds, cu_count() / kXcds * kXcds); }
 }  // namespace
 
 namespace {
-template <bool GATHER>
+template <bool GATHER, bool SAVE_GU>
 void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
-                  const int32_t* offsets, const void* packed_gu, void* a, bool decode,
+                  const int32_t* offsets, const void* packed_gu, void* a, void* gu, bool decode,
                   hipStream_t s) {
   if (decode) {
     const int nf32 = p.I / 32;
-    hipLaunchKernelGGL((decode_kernel<true, GATHER>), dim3(div_up(nf32, 4), p.E), dim3(256), 0,
-                       s, (const uint16_t*)xs, row_token, offsets, (const uint16_t*)packed_gu,
-                       (uint16_t*)a, p.H, p.I);
+    hipLaunchKernelGGL((decode_kernel<true, GATHER, SAVE_GU>), dim3(div_up(nf32, 4), p.E),
+                       dim3(256), 0, s, (const uint16_t*)xs, row_token, offsets,
+                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I, (uint16_t*)gu);
   } else {
-    hipLaunchKernelGGL((prefill_kernel<true, GATHER>), dim3(persistent_grid()), dim3(kThreads),
-                       0, s, (const uint16_t*)xs, row_token, offsets, p.E,
-                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I);
+    hipLaunchKernelGGL((prefill_kernel<true, GATHER, SAVE_GU>), dim3(persistent_grid()),
+                       dim3(kThreads), 0, s, (const uint16_t*)xs, row_token, offsets, p.E,
+                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I, (uint16_t*)gu);
   }
 }
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
-                               const int32_t* offsets, const void* packed_gu, void* a,
+                               const int32_t* offsets, const void* packed_gu, void* a, void* gu,
                                bool decode, hipStream_t s) {
-  if (row_token)
-    gate_up_bf16<true>(p, xs, row_token, offsets, packed_gu, a, decode, s);
+  if (row_token && gu)
+    gate_up_bf16<true, true>(p, xs, row_token, offsets, packed_gu, a, gu, decode, s);
+  else if (row_token)
+    gate_up_bf16<true, false>(p, xs, row_token, offsets, packed_gu, a, nullptr, decode, s);
+  else if (gu)
+    gate_up_bf16<false, true>(p, xs, nullptr, offsets, packed_gu, a, gu, decode, s);
   else
-    gate_up_bf16<false>(p, xs, nullptr, offsets, packed_gu, a, decode, s);
+    gate_up_bf16<false, false>(p, xs, nullptr, offsets, packed_gu, a, nullptr, decode, s);
   return hipGetLastError();
 }
 
@@ -601,20 +641,20 @@ hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
     if (row_token)
       hipLaunchKernelGGL((decode_kernel<false, true>), dim3(div_up(nf32 / 2, 4), E), dim3(256), 0,
                          s, (const uint16_t*)A, row_token, offsets, (const uint16_t*)packed_b,
-                         (uint16_t*)out, K, Nout);
+                         (uint16_t*)out, K, Nout, nullptr);
     else
       hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), E), dim3(256),
                          0, s, (const uint16_t*)A, nullptr, offsets, (const uint16_t*)packed_b,
-                         (uint16_t*)out, K, Nout);
+                         (uint16_t*)out, K, Nout, nullptr);
   } else {
     if (row_token)
       hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(persistent_grid()), dim3(kThreads),
                          0, s, (const uint16_t*)A, row_token, offsets, E,
-                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout);
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr);
     else
       hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()),
                          dim3(kThreads), 0, s, (const uint16_t*)A, nullptr, offsets, E,
-                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout);
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr);
   }
   return hipGetLastError();
 }
@@ -625,11 +665,11 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
     const int nf32 = p.H / 32;
     hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
                        0, s, (const uint16_t*)a, nullptr, offsets, (const uint16_t*)packed_d,
-                       (uint16_t*)yp, p.I, p.H);
+                       (uint16_t*)yp, p.I, p.H, nullptr);
   } else {
     hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()), dim3(kThreads),
                        0, s, (const uint16_t*)a, nullptr, offsets, p.E,
-                       (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H);
+                       (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H, nullptr);
   }
   return hipGetLastError();
 }

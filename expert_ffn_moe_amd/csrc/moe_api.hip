@@ -309,9 +309,10 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
 // Gate/up over the layout: rows xs[r], or token rows xs[row_token[r]] if row_token != NULL.
 // FP8: the input rows (T token rows, or T*k rows of xp) are quantised into f.xq first.
 // decode: which bf16 kernel family (ffn_use_decode of the problem the rows belong to).
+// gu (bf16 only): also store the pre-activations g|u.
 hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_token,
                        const int32_t* offsets, const void* pgu, void* a, const FfnScratch& f,
-                       bool decode, hipStream_t s) {
+                       bool decode, hipStream_t s, void* gu = nullptr) {
   if (is_fp8(p)) {
     const size_t tk = (size_t)p.T * p.k;
     const size_t rows = row_token ? (size_t)p.T : tk;
@@ -329,7 +330,7 @@ hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_
     return launch_gate_up_f32(p, (const float*)xs, row_token, offsets, (const float*)pgu,
                               (const float*)pgu + n, (float*)a, s);
   }
-  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, decode, s);
+  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, gu, decode, s);
 }
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
@@ -519,6 +520,19 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
                   ffn_use_decode(*p), as_stream(stream)));
 }
 
+int moe_expert_gate_up_gather_gu(const moe_problem* p, const void* x, const int32_t* row_token,
+                                 const int32_t* offsets, const void* packed_gate_up, void* a,
+                                 void* gu, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  if (!backward_supported(*p, false)) return MOE_ERR_UNSUPPORTED;
+  if (!x || !row_token || !offsets || !packed_gate_up || !a || !gu) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(packed_gate_up) || !aligned16(a) || !aligned16(gu))
+    return MOE_ERR_INVALID_ARG;
+  return status_of(run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, FfnScratch{},
+                               ffn_use_decode(*p), as_stream(stream), gu));
+}
+
 int moe_quantize_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, uint8_t* scales,
                      void* stream) {
   if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
@@ -622,8 +636,8 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
                        const void* w_router, const void* packed_gate_up,
                        const void* packed_down, const void* packed_bwd_gate_up,
                        const void* packed_bwd_down, const moe_saved_routing* saved,
-                       const void* yp, const void* dy, const moe_grads* grads, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       const void* yp, const void* gu, const void* dy, const moe_grads* grads,
+                       void* ws, size_t ws_bytes, void* stream) {
   int st = moe_problem_check(p);
   if (st != MOE_OK) return st;
   if (!backward_supported(*p, w_router != nullptr)) return MOE_ERR_UNSUPPORTED;
@@ -638,7 +652,7 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
       (!yp && !packed_down))
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(dy) || !aligned16(grads->dx) || (yp && !aligned16(yp)) ||
-      (w_router && !aligned16(w_router)))
+      (gu && !aligned16(gu)) || (w_router && !aligned16(w_router)))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
@@ -659,12 +673,15 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   // combine and routing backward
   if (err == hipSuccess) err = launch_combine_bwd(*p, dy, yp, R.topk_w, R.slot_to_row, B.dyp, dw, s);
   if (err == hipSuccess) err = launch_route_bwd(*p, logits, R.topk_ids, R.topk_w, dw, grads->dlogits, s);
-  // data gradients: da = dyp W_down^T; g|u recomputed; SwiGLU backward; dxp = dgu [Wg|Wu]^T
+  // data gradients: da = dyp W_down^T; g|u (saved, or recomputed); SwiGLU backward;
+  // dxp = dgu [Wg|Wu]^T
   if (err == hipSuccess)
     err = launch_gemm_bf16(E, B.dyp, nullptr, R.offsets, packed_bwd_down, B.da, H, I, dec, s);
-  if (err == hipSuccess)
+  if (err == hipSuccess && !gu) {
     err = launch_gemm_bf16(E, x, R.row_token, R.offsets, packed_gate_up, B.gu, H, 2 * I, dec, s);
-  if (err == hipSuccess) err = launch_swiglu_bwd(*p, B.gu, B.da, R.offsets, B.dgu, B.a, s);
+    gu = B.gu;
+  }
+  if (err == hipSuccess) err = launch_swiglu_bwd(*p, gu, B.da, R.offsets, B.dgu, B.a, s);
   if (err == hipSuccess)
     err = launch_gemm_bf16(E, B.dgu, nullptr, R.offsets, packed_bwd_gate_up, B.dxp, 2 * I, H,
                            dec, s);

@@ -125,9 +125,10 @@ hipError_t launch_pack_plain(int E, int K, int N, const void* w, void* packed, h
 // whole problem (a chunked layer decides once, so every chunk uses the same kernels).
 bool ffn_use_decode(const moe_problem& p);
 // Gate/up over the layout's rows: row r reads xs[r] (xp), or xs[row_token[r]] (token rows
-// x) when row_token is not NULL.
+// x) when row_token is not NULL.  gu, if not NULL, receives the pre-activations [rows, 2I]
+// exactly as launch_gemm_bf16 over the packed gate/up weights computes them.
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
-                               const int32_t* offsets, const void* packed_gu, void* a,
+                               const int32_t* offsets, const void* packed_gu, void* a, void* gu,
                                bool decode, hipStream_t s);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
                             const void* packed_d, void* yp, bool decode, hipStream_t s);

@@ -335,6 +335,15 @@ int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
  * the forward above (route -> capacity -> layout -> SwiGLU experts -> combine) for an
  * upstream gradient dy; the selection itself carries no gradient.
  *
+ * moe_expert_gate_up_gather_gu: moe_expert_gate_up_gather (bf16) that also stores the
+ *   pre-activations for the backward: gu [T*k, 2I] bf16, row r of the layout holding
+ *   g = x W_gate[e] and u = x W_up[e] in 32-column blocks that alternate (columns 64 b ..
+ *   64 b + 31: g columns 32 b .., the next 32: u columns 32 b ..), rounded from the same
+ *   fp32 accumulators that give a (a is bit for bit that of moe_expert_gate_up_gather).
+ *   Memory against time: the backward then skips its recompute of g|u.  Needs no
+ *   workspace.  MOE_ERR_UNSUPPORTED as moe_layer_backward (bf16, H % 128 == 0,
+ *   H <= 8192); MOE_ERR_INVALID_ARG for NULL or misaligned pointers.
+ *
  * moe_pack_weights_backward: the backward's operands, one-time like moe_pack_weights,
  *   from the natural bf16 weights: packed_bwd_gate_up (moe_packed_bytes(p,
  *   MOE_W_GATE_UP) bytes) holds [W_gate | W_up]^T, packed_bwd_down (moe_packed_bytes(p,
@@ -348,6 +357,9 @@ int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
  *     when yp is NULL), packed_bwd_*: from moe_pack_weights_backward,
  *   saved: the forward's routing outputs, yp [T*k, H] bf16: the forward's expert outputs
  *     (moe_expert_down), or NULL to recompute them,
+ *   gu [T*k, 2I] bf16: the forward's pre-activations from moe_expert_gate_up_gather_gu,
+ *     or NULL to recompute them (one grouped GEMM over the packed gate/up weights; the
+ *     saved ones have the same bits, so the gradients do not depend on the choice),
  *   dy [T, H] bf16.
  * Outputs (grads): dx [T, H] bf16; dw_gate, dw_up [E, H, I] and dw_down [E, I, H] f32
  *   (zero for experts without rows); dlogits [T, E] f32; dtopk_w [T, k] f32 or NULL;
@@ -378,12 +390,15 @@ typedef struct {
 int moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up,
                               const void* w_down, void* packed_bwd_gate_up,
                               void* packed_bwd_down, void* stream);
+int moe_expert_gate_up_gather_gu(const moe_problem* p, const void* x, const int32_t* row_token,
+                                 const int32_t* offsets, const void* packed_gate_up, void* a,
+                                 void* gu, void* stream);
 int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
                        const void* w_router, const void* packed_gate_up,
                        const void* packed_down, const void* packed_bwd_gate_up,
                        const void* packed_bwd_down, const moe_saved_routing* saved,
-                       const void* yp, const void* dy, const moe_grads* grads, void* ws,
-                       size_t ws_bytes, void* stream);
+                       const void* yp, const void* gu, const void* dy,
+                       const moe_grads* grads, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -40,6 +40,27 @@ def _sigmoid(z):
     return 1.0 / (1.0 + np.exp(-z))
 
 
+def gate_up_rows(x, row_token, offsets, w_gate, w_up, experts: Optional[np.ndarray] = None):
+    """The pre-activations the backward reuses, per layout row r of expert e (token
+    t = row_token[r]): g[r] = x[t] Wg[e] and u[r] = x[t] Wu[e] in fp64 (the forward's
+    definition above; LightLLM PR #1687 walkthrough: the gate/up GEMM that silu_and_mul
+    follows).  Only the rows of `experts` (default: all) are filled.  Returns (g, u), each
+    [offsets[E], I]."""
+    offsets = np.asarray(offsets, np.int64)
+    E, I = w_gate.shape[0], w_gate.shape[2]
+    N = int(offsets[-1])
+    g = np.zeros((N, I))
+    u = np.zeros((N, I))
+    xd = _f64(x)
+    for e in (range(E) if experts is None else experts):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            xe = xd[np.asarray(row_token[r0:r1], np.int64)]
+            g[r0:r1] = xe @ _f64(w_gate[e])
+            u[r0:r1] = xe @ _f64(w_up[e])
+    return g, u
+
+
 def layer_backward(x, logits, w_gate, w_up, w_down, k: int, dy, capacity_: int = 0,
                    renormalize: int = 1, w_router: Optional[np.ndarray] = None,
                    experts: Optional[np.ndarray] = None, tokens: Optional[np.ndarray] = None):

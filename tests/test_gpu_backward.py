@@ -87,9 +87,27 @@ def run_case(wl, router=False, tokens=None, experts=None):
                          w_router=wr)
     g2 = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=None,
                           w_router=wr)
+    # the forward's gate/up with the pre-activations saved: the same a, and the backward
+    # on them gives the same bits as with its own recompute
+    a1 = m.expert_gate_up_gather(p, inp["x"], routing["row_token"], routing["offsets"], pgu)
+    a2, gu = m.expert_gate_up_gather_gu(p, inp["x"], routing["row_token"], routing["offsets"],
+                                        pgu)
+    g3 = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=yp,
+                          w_router=wr, gu=gu)
     torch.cuda.synchronize()
     for n in g:
         assert torch.equal(g[n], g2[n]), f"{n}: recomputed yp differs"
+        assert torch.equal(g[n], g3[n]), f"{n}: saved g|u differs from the recomputed"
+    N = int(routing["offsets"][-1].item())
+    assert torch.equal(a1[:N], a2[:N]), "a of the g|u-saving gate/up differs"
+    exps_gu = np.arange(p.E) if experts is None else np.asarray(experts)
+    rg, ru = ob.gate_up_rows(host(inp["x"]), host(routing["row_token"]), host(routing["offsets"]),
+                             host(inp["w_gate"]), host(inp["w_up"]), experts=exps_gu)
+    offs = host(routing["offsets"])
+    rows = np.concatenate([np.arange(offs[e], offs[e + 1]) for e in exps_gu]).astype(np.int64)
+    gu_h = as_f64(host(gu))[rows].reshape(len(rows), p.I // 32, 2, 32)
+    check("g (saved)", gu_h[:, :, 0, :].reshape(len(rows), p.I), rg[rows])
+    check("u (saved)", gu_h[:, :, 1, :].reshape(len(rows), p.I), ru[rows])
     ref = ob.layer_backward(host(inp["x"]), host(logits), host(inp["w_gate"]), host(inp["w_up"]),
                             host(inp["w_down"]), p.k, host(dy), p.capacity, p.renormalize,
                             w_router=None if wr is None else host(wr), experts=experts,
@@ -141,6 +159,13 @@ def test_backward_rejects_what_it_does_not_handle():
     w = torch.zeros(4, 192, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(m.MoeError) as ei:
         m.pack_weights_backward(p, w, w, w.transpose(1, 2).contiguous())
+    assert ei.value.status == m.MOE_ERR_UNSUPPORTED
+    x = torch.zeros(8, 192, dtype=torch.bfloat16, device=DEV)
+    rt = torch.zeros(16, dtype=torch.int32, device=DEV)
+    off = torch.zeros(5, dtype=torch.int32, device=DEV)
+    pgu = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(m.MoeError) as ei:
+        m.expert_gate_up_gather_gu(p, x, rt, off, pgu)
     assert ei.value.status == m.MOE_ERR_UNSUPPORTED
 
 

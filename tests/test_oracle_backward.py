@@ -11,6 +11,7 @@ import pytest
 import torch
 
 import oracle
+import synth
 from oracle import backward as ob
 
 
@@ -141,3 +142,27 @@ def test_backward_token_subset():
         assert np.allclose(sub[n][toks], full[n][toks], rtol=1e-13, atol=1e-13), n
     for n in ("dw_gate", "dw_up", "dw_down"):
         assert np.allclose(sub[n][0], full[n][2], rtol=1e-13, atol=1e-13), n
+
+
+def test_gate_up_rows_gives_the_ffn_activation():
+    """silu(g) * u from the backward's pre-activations (numpy) equals the activation a of
+    the C oracle's expert FFN on the same rows, and rows of experts left out stay zero."""
+    rng = np.random.default_rng(11)
+    T, H, E, k, I = 40, 64, 5, 2, 96
+    x = synth.bf16_bits(torch.from_numpy(rng.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16))
+    wg, wu = (synth.bf16_bits(torch.from_numpy(rng.standard_normal((E, H, I), dtype=np.float32) * 0.1)
+                              .to(torch.bfloat16)) for _ in range(2))
+    wd = synth.bf16_bits(torch.from_numpy(rng.standard_normal((E, I, H), dtype=np.float32) * 0.1)
+                         .to(torch.bfloat16))
+    ids, _ = oracle.route(rng.standard_normal((T, E)).astype(np.float32), k)
+    lay = oracle.layout(ids, None, E)
+    N = lay["N"]
+    g, u = ob.gate_up_rows(x, lay["row_token"], lay["offsets"], wg, wu)
+    rexp = (np.searchsorted(lay["offsets"], np.arange(N), side="right") - 1).astype(np.int32)
+    _, a = oracle.ffn_rows(oracle.gather(x, lay["row_token"], N), rexp, wg, wu, wd, want_a=True)
+    ref = g / (1.0 + np.exp(-g)) * u
+    assert np.abs(ref - a).max() <= 1e-12 * np.abs(a).max()
+    g2, u2 = ob.gate_up_rows(x, lay["row_token"], lay["offsets"], wg, wu, experts=[1, 3])
+    mine = np.isin(rexp, [1, 3])
+    assert np.array_equal(g2[mine], g[mine]) and np.array_equal(u2[mine], u[mine])
+    assert not g2[~mine].any() and not u2[~mine].any()
