@@ -105,7 +105,7 @@ def run_case(wl, router=False, tokens=None, experts=None):
                              host(inp["w_gate"]), host(inp["w_up"]), experts=exps_gu)
     offs = host(routing["offsets"])
     rows = np.concatenate([np.arange(offs[e], offs[e + 1]) for e in exps_gu]).astype(np.int64)
-    gu_h = as_f64(host(gu))[rows].reshape(len(rows), p.I // 32, 2, 32)
+    gu_h = as_f64(host(gu)[rows]).reshape(len(rows), p.I // 32, 2, 32)  # rows >= N: unset
     check("g (saved)", gu_h[:, :, 0, :].reshape(len(rows), p.I), rg[rows])
     check("u (saved)", gu_h[:, :, 1, :].reshape(len(rows), p.I), ru[rows])
     ref = ob.layer_backward(host(inp["x"]), host(logits), host(inp["w_gate"]), host(inp["w_up"]),
