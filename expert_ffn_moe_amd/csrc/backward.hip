@@ -80,39 +80,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                   : (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
 }
 
-// SwiGLU backward on the interleaved gate|up rows (32-column blocks of g and u alternate),
-// for the layout's rows r < offsets[E]: dgu (same interleaving) and the recomputed a.
-__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint4* __restrict__ gu,
-                                                         const uint4* __restrict__ da,
-                                                         const int32_t* __restrict__ nrows,
-                                                         int I, uint4* __restrict__ dgu,
-                                                         uint4* __restrict__ a) {
-  const int per_row = I / 8;
-  const int64_t total = (int64_t)(*nrows) * per_row;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
-       q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = q / per_row;
-    const int c8 = (int)(q - r * per_row);
-    const int i0 = 8 * c8, b = i0 >> 5, j0 = i0 & 31;
-    const int64_t gv = (r * 2 * I + 64 * b + j0) / 8;  // uint4 index of g; u is 4 further
-    float g[8], u[8], d[8], og[8], ou[8], oa[8];
-    unpack8(gu[gv], g);
-    unpack8(gu[gv + 4], u);
-    unpack8(da[r * per_row + c8], d);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float s = 1.0f / (1.0f + __expf(-g[i]));
-      const float silu = g[i] * s;
-      oa[i] = silu * u[i];
-      ou[i] = d[i] * silu;
-      og[i] = d[i] * u[i] * s * (1.0f + g[i] * (1.0f - s));
-    }
-    dgu[gv] = pack8(og);
-    dgu[gv + 4] = pack8(ou);
-    a[r * per_row + c8] = pack8(oa);
-  }
-}
-
 // poff[e] = sum over e' < e of the count of e' rounded up to a multiple of gran, poff[E]
 // the total (E <= 1024, one block).
 __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __restrict__ offsets,
@@ -133,29 +100,24 @@ __global__ __launch_bounds__(1024) void pad_offsets_kernel(const int32_t* __rest
   if (e == E - 1) poff[E] = s[e];
 }
 
-// dst[c][q] for the padded columns q of a block: column q = poff[e] + i holds src row
-// offsets[e] + i (through row_map if given) while i < count_e, zeros after.  A block takes
-// 64 destination columns x up to kTransposeChunks chunks of 64 values of c: it finds the
-// source rows once, loads every chunk (128 contiguous bytes of each source row per chunk,
-// all in flight together), then per chunk stores 64 destination rows (128 contiguous bytes
-// each) through LDS.
-// PACKED: dst in matrix-core operand order instead (the weight-gradient GEMM's B operand):
-// 1 KiB blocks of 32 values of c x 16 columns q, ordered [c / 32][q / 16]; piece
-// (c % 32) + 32 h of a block holds columns 8 h .. + 7 of value c.
+// Transposes into the weight gradients' operand layouts.  A block owns 64 destination
+// columns q0 .. q0 + 63 of the padded layout: column q = poff[e] + i is row offsets[e] + i of
+// the source while i < count_e, and zeros after.  Values pass through an LDS tile
+// [64 columns][64 values] (bf16 pairs, padded rows): thread (j, part) = (tid / 4, tid % 4)
+// puts values 16 part .. + 15 of column j, then takes value tid / 4 for columns
+// 16 part .. + 15 and stores them as two 16-byte pieces:
+//  plain : dst[c][q], row stride npad;
+//  PACKED: matrix-core operand order (the weight-gradient GEMM's B operand), 1 KiB blocks
+//          of 32 values of c x 16 columns q, ordered [c / 32][q / 16]; piece (c % 32) + 32 h
+//          of a block holds columns 8 h .. + 7 of value c.
 constexpr int kTransposeChunks = 4;
+typedef uint32_t TileRow[33];
 
-template <bool PACKED>
-__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
-                                                            const int32_t* __restrict__ row_map,
-                                                            const int32_t* __restrict__ offsets,
-                                                            const int32_t* __restrict__ poff,
-                                                            int E, int C, int64_t npad,
-                                                            uint16_t* __restrict__ dst) {
-  __shared__ uint32_t tile[64][33];  // [destination column][pairs of c], padded row
-  __shared__ int srow[64];
-  const int q0 = blockIdx.x * 64, cb = blockIdx.y * 64 * kTransposeChunks;
-  const int nch = min(kTransposeChunks, (C - cb) / 64);
-  if (q0 >= poff[E]) return;  // block-uniform
+// Source row of each of the block's 64 columns (-1: padding), into srow.
+__device__ __forceinline__ void tile_rows(const int32_t* __restrict__ row_map,
+                                          const int32_t* __restrict__ offsets,
+                                          const int32_t* __restrict__ poff, int E, int q0,
+                                          int* srow) {
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int q = q0 + tid;
@@ -167,8 +129,57 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
     const int r = offsets[lo] + (q - poff[lo]);
     srow[tid] = r < offsets[lo + 1] ? (row_map ? row_map[r] : r) : -1;
   }
+}
+
+__device__ __forceinline__ void tile_put(TileRow* tile, int j, int part, const uint4& v0,
+                                         const uint4& v1) {
+  uint32_t* t = &tile[j][8 * part];
+  t[0] = v0.x; t[1] = v0.y; t[2] = v0.z; t[3] = v0.w;
+  t[4] = v1.x; t[5] = v1.y; t[6] = v1.z; t[7] = v1.w;
+}
+
+// Stores tile value cc (columns 16 part .. + 15) as destination value c.
+template <bool PACKED>
+__device__ __forceinline__ void tile_store(const TileRow* tile, int cc, int part, int c, int q0,
+                                           int64_t npad, uint16_t* __restrict__ dst) {
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t a = tile[16 * part + 2 * i][cc >> 1], b = tile[16 * part + 2 * i + 1][cc >> 1];
+    const int sh = 16 * (cc & 1);
+    w[i] = ((a >> sh) & 0xFFFF) | (((b >> sh) & 0xFFFF) << 16);
+  }
+  if constexpr (PACKED) {
+    uint4* blk = reinterpret_cast<uint4*>(dst) +
+                 ((int64_t)(c >> 5) * (npad >> 4) + (q0 >> 4) + part) * 64;
+    blk[c & 31] = make_uint4(w[0], w[1], w[2], w[3]);
+    blk[(c & 31) + 32] = make_uint4(w[4], w[5], w[6], w[7]);
+  } else {
+    uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)c * npad + q0 + 16 * part);
+    d[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
+// dst = src [rows, C] transposed into the padded layout (rows through row_map if given).
+// A block takes up to kTransposeChunks chunks of 64 values of c: the source rows are found
+// once and every chunk's loads (128 contiguous bytes of a source row each) are in flight
+// together.
+template <bool PACKED>
+__global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __restrict__ src,
+                                                            const int32_t* __restrict__ row_map,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ poff,
+                                                            int E, int C, int64_t npad,
+                                                            uint16_t* __restrict__ dst) {
+  __shared__ TileRow tile[64];
+  __shared__ int srow[64];
+  const int q0 = blockIdx.x * 64, cb = blockIdx.y * 64 * kTransposeChunks;
+  if (q0 >= poff[E]) return;  // block-uniform
+  const int nch = min(kTransposeChunks, (C - cb) / 64);
+  tile_rows(row_map, offsets, poff, E, q0, srow);
   __syncthreads();
-  const int j = tid >> 2, part = tid & 3;  // load: column j, values 16 part .. + 15 of a chunk
+  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
   uint4 v[kTransposeChunks][2];
   {
     const int r = srow[j];
@@ -187,32 +198,95 @@ __global__ __launch_bounds__(256) void transpose_pad_kernel(const uint16_t* __re
   for (int ch = 0; ch < kTransposeChunks; ++ch) {
     if (ch >= nch) break;  // block-uniform
     if (ch > 0) __syncthreads();  // the previous chunk's reads of the tile are done
-    {
-      uint32_t* t = &tile[j][8 * part];
-      t[0] = v[ch][0].x; t[1] = v[ch][0].y; t[2] = v[ch][0].z; t[3] = v[ch][0].w;
-      t[4] = v[ch][1].x; t[5] = v[ch][1].y; t[6] = v[ch][1].z; t[7] = v[ch][1].w;
-    }
+    tile_put(tile, j, part, v[ch][0], v[ch][1]);
     __syncthreads();
-    const int c0 = cb + 64 * ch;
-    const int cc = tid >> 2;  // store: value c0 + cc, columns 16 part .. + 15
-    uint32_t w[8];
+    tile_store<PACKED>(tile, tid >> 2, part, cb + 64 * ch + (tid >> 2), q0, npad, dst);
+  }
+}
+
+// SwiGLU backward on the interleaved gate|up rows (32-column blocks of g and u alternate),
+// fused with the transposes its outputs need for the weight gradients.  Grid and column
+// mapping as transpose_pad_kernel over the I values of a row, kSwigluChunks chunks of 64
+// per block; per value, with s = sigma(g):
+//   a = silu(g) u,  du = da silu(g),  dg = da u s (1 + g (1 - s))
+// written as dgu (row-major, interleaved like gu: the data-gradient GEMM's input), dguT
+// (packed, 2I values: the gate/up weight gradient's B operand) and aT (plain, I values: the
+// down weight gradient's A operand); padding columns get zeros.
+constexpr int kSwigluChunks = 2;
+__global__ __launch_bounds__(256) void swiglu_bwd_kernel(const uint16_t* __restrict__ gu,
+                                                         const uint16_t* __restrict__ da,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ poff,
+                                                         int E, int I, int64_t npad,
+                                                         uint16_t* __restrict__ dgu,
+                                                         uint16_t* __restrict__ dguT,
+                                                         uint16_t* __restrict__ aT) {
+  __shared__ TileRow tg[64], tu[64], ta[64];
+  __shared__ int srow[64];
+  const int q0 = blockIdx.x * 64, cb = blockIdx.y * 64 * kSwigluChunks;
+  if (q0 >= poff[E]) return;  // block-uniform
+  const int nch = min(kSwigluChunks, (I - cb) / 64);
+  tile_rows(nullptr, offsets, poff, E, q0, srow);
+  __syncthreads();
+  const int tid = threadIdx.x, j = tid >> 2, part = tid & 3;
+  const int r = srow[j];
+  uint4 vg[kSwigluChunks][2], vu[kSwigluChunks][2], vd[kSwigluChunks][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t a = tile[16 * part + 2 * i][cc >> 1], b = tile[16 * part + 2 * i + 1][cc >> 1];
-      const int sh = 16 * (cc & 1);
-      w[i] = ((a >> sh) & 0xFFFF) | (((b >> sh) & 0xFFFF) << 16);
+  for (int ch = 0; ch < kSwigluChunks; ++ch) {
+    vg[ch][0] = vg[ch][1] = vu[ch][0] = vu[ch][1] = vd[ch][0] = vd[ch][1] = make_uint4(0, 0, 0, 0);
+    if (r >= 0 && ch < nch) {
+      const int i0 = cb + 64 * ch + 16 * part;  // values i0 .. + 15, inside one 32-block
+      const uint4* gp = reinterpret_cast<const uint4*>(gu + (int64_t)r * 2 * I + 64 * (i0 >> 5) +
+                                                       (i0 & 31));
+      const uint4* dp = reinterpret_cast<const uint4*>(da + (int64_t)r * I + i0);
+      vg[ch][0] = gp[0];
+      vg[ch][1] = gp[1];
+      vu[ch][0] = gp[4];  // the up values sit 32 columns further
+      vu[ch][1] = gp[5];
+      vd[ch][0] = dp[0];
+      vd[ch][1] = dp[1];
     }
-    if constexpr (PACKED) {
-      const int c = c0 + cc;
-      uint4* blk = reinterpret_cast<uint4*>(dst) +
-                   ((int64_t)(c >> 5) * (npad >> 4) + (q0 >> 4) + part) * 64;
-      blk[c & 31] = make_uint4(w[0], w[1], w[2], w[3]);
-      blk[(c & 31) + 32] = make_uint4(w[4], w[5], w[6], w[7]);
-    } else {
-      uint4* d = reinterpret_cast<uint4*>(dst + (int64_t)(c0 + cc) * npad + q0 + 16 * part);
-      d[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      d[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+#pragma unroll
+  for (int ch = 0; ch < kSwigluChunks; ++ch) {
+    if (ch >= nch) break;  // block-uniform
+    if (ch > 0) __syncthreads();  // the previous chunk's reads of the tiles are done
+    uint4 og[2], ou[2], oa[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float g[8], u[8], d[8], fg[8], fu[8], fa[8];
+      unpack8(vg[ch][h], g);
+      unpack8(vu[ch][h], u);
+      unpack8(vd[ch][h], d);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float s = 1.0f / (1.0f + __expf(-g[i]));
+        const float silu = g[i] * s;
+        fa[i] = silu * u[i];
+        fu[i] = d[i] * silu;
+        fg[i] = d[i] * u[i] * s * (1.0f + g[i] * (1.0f - s));
+      }
+      og[h] = pack8(fg);
+      ou[h] = pack8(fu);
+      oa[h] = pack8(fa);
     }
+    if (r >= 0) {
+      const int i0 = cb + 64 * ch + 16 * part;
+      uint4* gp = reinterpret_cast<uint4*>(dgu + (int64_t)r * 2 * I + 64 * (i0 >> 5) + (i0 & 31));
+      gp[0] = og[0];
+      gp[1] = og[1];
+      gp[4] = ou[0];
+      gp[5] = ou[1];
+    }
+    tile_put(tg, j, part, og[0], og[1]);
+    tile_put(tu, j, part, ou[0], ou[1]);
+    tile_put(ta, j, part, oa[0], oa[1]);
+    __syncthreads();
+    const int cc = tid >> 2, i = cb + 64 * ch + cc;  // value i, columns 16 part .. + 15
+    const int c = 64 * (i >> 5) + (i & 31);          // its gate column in the interleaved 2I
+    tile_store<true>(tg, cc, part, c, q0, npad, dguT);
+    tile_store<true>(tu, cc, part, c + 32, q0, npad, dguT);
+    tile_store<false>(ta, cc, part, i, q0, npad, aT);
   }
 }
 
@@ -238,11 +312,12 @@ hipError_t launch_combine_bwd(const moe_problem& p, const void* dy, const void* 
 }
 
 hipError_t launch_swiglu_bwd(const moe_problem& p, const void* gu, const void* da,
-                             const int32_t* offsets, void* dgu, void* a, hipStream_t s) {
-  const int64_t work = (int64_t)p.T * p.k * (p.I / 8);
-  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3(grid_for(work, 256)), dim3(256), 0, s,
-                     (const uint4*)gu, (const uint4*)da, offsets + p.E, p.I, (uint4*)dgu,
-                     (uint4*)a);
+                             const int32_t* offsets, const int32_t* poff, int64_t npad, void* dgu,
+                             void* dguT, void* aT, hipStream_t s) {
+  const dim3 grid((unsigned)(npad / 64), (unsigned)div_up(p.I / 64, kSwigluChunks));
+  hipLaunchKernelGGL(swiglu_bwd_kernel, grid, dim3(256), 0, s, (const uint16_t*)gu,
+                     (const uint16_t*)da, offsets, poff, p.E, p.I, npad, (uint16_t*)dgu,
+                     (uint16_t*)dguT, (uint16_t*)aT);
   return hipGetLastError();
 }
 

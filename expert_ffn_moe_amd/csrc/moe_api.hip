@@ -182,7 +182,7 @@ bool router_bwd_ok(const moe_problem& p) { return p.E % 64 == 0; }
 
 struct BwdScratch {
   float* dw;       // d topk_w when the caller does not want it
-  void *dyp, *da, *gu, *dgu, *a, *dxp, *yp;
+  void *dyp, *da, *gu, *dgu, *dxp, *yp;
   FfnScratch ffn;  // the yp recompute's intermediate
   int32_t* poff;
   int64_t npad;    // row stride of the transposes
@@ -201,7 +201,6 @@ BwdScratch carve_backward(Carve& c, const moe_problem& p, bool router) {
   B.da = c.take<uint16_t>(tk * p.I);
   B.gu = c.take<uint16_t>(tk * 2 * p.I);
   B.dgu = c.take<uint16_t>(tk * 2 * p.I);
-  B.a = c.take<uint16_t>(tk * p.I);
   B.dxp = c.take<uint16_t>(tk * p.H);
   B.yp = c.take<uint16_t>(tk * p.H);
   B.ffn = carve_ffn(c, p);
@@ -681,7 +680,9 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
     err = launch_gemm_bf16(E, x, R.row_token, R.offsets, packed_gate_up, B.gu, H, 2 * I, dec, s);
     gu = B.gu;
   }
-  if (err == hipSuccess) err = launch_swiglu_bwd(*p, gu, B.da, R.offsets, B.dgu, B.a, s);
+  if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, 64, B.poff, s);
+  if (err == hipSuccess)
+    err = launch_swiglu_bwd(*p, gu, B.da, R.offsets, B.poff, B.npad, B.dgu, B.dguT, B.aT, s);
   if (err == hipSuccess)
     err = launch_gemm_bf16(E, B.dgu, nullptr, R.offsets, packed_bwd_gate_up, B.dxp, 2 * I, H,
                            dec, s);
@@ -708,15 +709,11 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   if (err == hipSuccess)
     err = launch_combine(*p, B.dxp, nullptr, R.slot_to_row, dxr, grads->dx, s);
   // weight gradients over each expert's rows
-  if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, 64, B.poff, s);
+  // (aT and dguT came with the SwiGLU backward)
   if (err == hipSuccess)
     err = launch_transpose_pad(x, R.row_token, R.offsets, B.poff, E, H, B.npad, false, B.xT, s);
   if (err == hipSuccess)
-    err = launch_transpose_pad(B.a, nullptr, R.offsets, B.poff, E, I, B.npad, false, B.aT, s);
-  if (err == hipSuccess)
     err = launch_transpose_pad(B.dyp, nullptr, R.offsets, B.poff, E, H, B.npad, true, B.dypT, s);
-  if (err == hipSuccess)
-    err = launch_transpose_pad(B.dgu, nullptr, R.offsets, B.poff, E, 2 * I, B.npad, true, B.dguT, s);
   if (err == hipSuccess)
     err = launch_wgrad_bf16(B.aT, B.dypT, B.poff, E, I, H, B.npad, false, grads->dw_down,
                             nullptr, s);

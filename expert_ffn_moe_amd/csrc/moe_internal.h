@@ -98,8 +98,12 @@ hipError_t launch_one_expert_offsets(int32_t* off, int n, hipStream_t s);
 hipError_t launch_combine_bwd(const moe_problem& p, const void* dy, const void* yp,
                               const float* w, const int32_t* slot_to_row, void* dyp, float* dw,
                               hipStream_t s);
+// SwiGLU backward from g|u and da (both [T*k, .] in the layout): dgu (row-major, gu's
+// interleaving) and, in the padded layout of poff / npad (launch_pad_offsets with gran 64),
+// dguT packed like launch_transpose_pad's packed form and aT plain.
 hipError_t launch_swiglu_bwd(const moe_problem& p, const void* gu, const void* da,
-                             const int32_t* offsets, void* dgu, void* a, hipStream_t s);
+                             const int32_t* offsets, const int32_t* poff, int64_t npad, void* dgu,
+                             void* dguT, void* aT, hipStream_t s);
 // poff[e]: the exclusive scan of the counts rounded up to a multiple of gran (16 or 64).
 hipError_t launch_pad_offsets(const int32_t* offsets, int E, int gran, int32_t* poff,
                               hipStream_t s);
