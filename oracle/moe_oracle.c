@@ -538,6 +538,9 @@ int orc_ue8m0(double amax) {
  * 1 bf16, 2 f64. */
 void orc_quant_rows(int64_t nrows, int ncols, int in_dtype, const void* in, uint8_t* codes,
                     uint8_t* scales) {
+  /* rows are independent: spread over threads when there are many (inside another
+   * parallel region this runs on the calling thread) */
+#pragma omp parallel for schedule(static) if (nrows >= 256)
   for (int64_t r = 0; r < nrows; ++r)
     for (int b = 0; b < ncols / ORC_QB; ++b) {
       double v[ORC_QB], amax = 0.0;

@@ -1,7 +1,7 @@
 """GPU parity of the backward pass (moe_layer_backward) against the oracle's fp64 chain
 rule (oracle/backward.py, itself pinned by finite differences and autograd).
 
-Bar: every gradient normwise, max|gpu - ref| <= 3e-2 max|ref| over the checked entries
+Bar: every gradient normwise, max|gpu - ref| <= 2e-2 max|ref| over the checked entries
 (bf16 operands and bf16 intermediate gradients -- dyp, da, [dg | du], dxp and the
 recomputed g, u, a -- each rounded at 2^-9, fp32 accumulation); the routing used by the
 backward is the forward's, which is bit-exact against the oracle (tested elsewhere).  The
@@ -19,7 +19,7 @@ from synth import Workload
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-TOL = 3e-2
+TOL = 2e-2
 
 
 def say(*a):
@@ -75,7 +75,10 @@ def check(name, got, ref):
     assert err <= TOL * scale, (name, err, scale)
 
 
-def run_case(wl, router=False, tokens=None, experts=None):
+def run_case(wl, router=False, tokens=None, experts=None, variants=True):
+    """variants: also run the backward with yp recomputed and with the forward's saved g|u
+    and compare them bit for bit (three sets of weight gradients in device memory at once;
+    the largest shape runs only the saved-g|u backward)."""
     m = moe()
     p = m.Problem.of(wl)
     inp = synth.make_inputs(wl, DEV)
@@ -83,23 +86,27 @@ def run_case(wl, router=False, tokens=None, experts=None):
     pgu, pd, routing, yp, logits = forward(p, inp, wr)
     pbgu, pbd = m.pack_weights_backward(p, inp["w_gate"], inp["w_up"], inp["w_down"])
     dy = make_dy(wl, DEV)
-    g = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=yp,
-                         w_router=wr)
-    g2 = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=None,
-                          w_router=wr)
-    # the forward's gate/up with the pre-activations saved: the same a, and the backward
-    # on them gives the same bits as with its own recompute
+    # the forward's gate/up with the pre-activations saved: the same a
     a1 = m.expert_gate_up_gather(p, inp["x"], routing["row_token"], routing["offsets"], pgu)
     a2, gu = m.expert_gate_up_gather_gu(p, inp["x"], routing["row_token"], routing["offsets"],
                                         pgu)
-    g3 = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=yp,
-                          w_router=wr, gu=gu)
     torch.cuda.synchronize()
-    for n in g:
-        assert torch.equal(g[n], g2[n]), f"{n}: recomputed yp differs"
-        assert torch.equal(g[n], g3[n]), f"{n}: saved g|u differs from the recomputed"
     N = int(routing["offsets"][-1].item())
     assert torch.equal(a1[:N], a2[:N]), "a of the g|u-saving gate/up differs"
+    del a1, a2
+    g = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy, yp=yp,
+                         w_router=wr, gu=gu)
+    torch.cuda.synchronize()
+    if variants:
+        # the backward on the saved g|u gives the same bits as with its own recompute, and
+        # recomputing yp changes nothing either
+        for yp_in, gu_in, what in ((yp, None, "recomputed g|u"), (None, gu, "recomputed yp")):
+            g2 = m.layer_backward(p, inp["x"], logits, pgu, pd, pbgu, pbd, routing, dy,
+                                  yp=yp_in, w_router=wr, gu=gu_in)
+            torch.cuda.synchronize()
+            for n in g:
+                assert torch.equal(g[n], g2[n]), f"{n}: {what} differs"
+            del g2
     exps_gu = np.arange(p.E) if experts is None else np.asarray(experts)
     rg, ru = ob.gate_up_rows(host(inp["x"]), host(routing["row_token"]), host(routing["offsets"]),
                              host(inp["w_gate"]), host(inp["w_up"]), experts=exps_gu)
@@ -118,8 +125,9 @@ def run_case(wl, router=False, tokens=None, experts=None):
     check("dx", as_f64(host(g["dx"]))[toks], ref["dx"][toks])
     check("dtopk_w", host(g["dtopk_w"])[toks], ref["dtopk_w"][toks])
     check("dlogits", host(g["dlogits"])[toks], ref["dlogits"][toks])
-    for n in ("dw_gate", "dw_up", "dw_down"):
-        check(n, host(g[n])[exps], ref[n])
+    sel = torch.as_tensor(exps, device=DEV)
+    for n in ("dw_gate", "dw_up", "dw_down"):  # (only the checked experts leave the device)
+        check(n, host(g[n].index_select(0, sel)), ref[n])
     if router and tokens is None:
         check("dw_router", host(g["dw_router"]), ref["dw_router"])
 
@@ -169,11 +177,12 @@ def test_backward_rejects_what_it_does_not_handle():
     assert ei.value.status == m.MOE_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "dsv3_decode", "glm_skew_cap"])
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b", "dsv3_decode", "glm_skew_cap", "dsv3_prefill"])
 def test_backward_full_size(name):
     wl = synth.WORKLOADS[name]
     say(f"case backward {name}: T={wl.T} H={wl.H} E={wl.E} k={wl.k} I={wl.I} C={wl.capacity}")
     rng = np.random.default_rng(wl.seed)
     tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 6, replace=False)]))
     experts = np.unique(rng.choice(wl.E, 2, replace=False))
-    run_case(wl, tokens=tokens, experts=experts)
+    # dsv3_prefill: 45 GB of fp32 weight gradients per backward call, so one call
+    run_case(wl, tokens=tokens, experts=experts, variants=name != "dsv3_prefill")

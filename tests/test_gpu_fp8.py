@@ -7,10 +7,13 @@ Bar:
     accumulation error of g and u (the oracle's is exact), which is large relative to a
     where g or u nearly cancel, so a code may land a step or more away from the oracle's.
     Checked element by element: dequant(a_gpu) is within half an E4M3 step of the exact
-    value plus the propagated accumulation bound (EPS_ACC = 2^-12 of the sum of |terms|
-    for g and u: the worst case measured for the scaled matrix-core instruction was
-    1.45e-4, fp32 summation of K terms adds at most K * 2^-24 of it); scales differ from
-    the oracle's by at most one; at most 1% of codes and of scales differ at all;
+    value plus the propagated accumulation bound eps_acc(K) * sum|terms| for g and u
+    (K = H terms, each an exact product of two E4M3 values and two power-of-two scales;
+    any order of floating-point summation of K terms errs by at most
+    gamma_{K-1} = (K-1) u / (1 - (K-1) u) of the sum of their magnitudes, taken here with
+    u = 2^-23 so that the bound holds whether the adders round to nearest or truncate);
+    scales differ from the oracle's by at most one; at most 1% of codes and of scales
+    differ at all;
   * yp and y: max|gpu - ref| <= 2e-2 * max|ref|, ref the oracle's fp64 result on the
     same quantised operands (bf16 output rounding is 2^-9 relative; the rest is the
     accumulation order and the rare adjacent-code roundings above).
@@ -57,7 +60,12 @@ def normwise(got_bits: np.ndarray, ref: np.ndarray):
     return err <= TOL * scale, err, scale
 
 
-EPS_ACC = 2.0 ** -12  # accumulation error bound, relative to the sum of |terms|
+def eps_acc(K: int) -> float:
+    """Error bound of a K-term floating-point sum relative to the sum of the terms'
+    magnitudes, gamma_{K-1} with unit roundoff 2^-23 (fp32 summation, rounding to nearest
+    or toward zero; the terms are exact products)."""
+    ku = (K - 1) * 2.0 ** -23
+    return ku / (1.0 - ku)
 
 
 def e4m3_quantum(v: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
@@ -69,12 +77,14 @@ def e4m3_quantum(v: np.ndarray, scale_bytes: np.ndarray) -> np.ndarray:
     return np.exp2(x - 3 + e)
 
 
-def check_intermediate(codes_g, scales_g, codes_o, scales_o, a_exact, g, u, sg, su):
+def check_intermediate(codes_g, scales_g, codes_o, scales_o, a_exact, g, u, sg, su, K):
     """The quantised intermediate against the oracle (rows x I):
     every GPU element lies within half an E4M3 step (at its own scale) of a value that the
     fp32 accumulation could have produced: |dequant(a_gpu) - a| <= q/2 + da, with a the
-    exact fp64 SwiGLU value, da = |d silu(g)/dg * u| * EPS_ACC * sum|g terms|
-    + |silu(g)| * EPS_ACC * sum|u terms| + 1e-5 |a|; scales differ by at most one."""
+    exact fp64 SwiGLU value, da = |d silu(g)/dg * u| * eps * sum|g terms|
+    + |silu(g)| * eps * sum|u terms| + 1e-5 |a|, eps = eps_acc(K); scales differ by at
+    most one."""
+    EPS_ACC = eps_acc(K)
     ds = scales_g.astype(np.int64) - scales_o.astype(np.int64)
     assert np.abs(ds).max(initial=0) <= 1, "a: scale off by more than one"
     sc = np.repeat(scales_g, oracle.QBLOCK, axis=1)
@@ -177,8 +187,10 @@ def oracle_weights(inp, experts):
             for n in ("w_gate", "w_up", "w_down")]
 
 
-def check_fp8_ffn(p, inp, g, rows=None, tokens=None):
-    """a and yp on `rows`, y on `tokens` (None: all) against the oracle."""
+def check_fp8_ffn(p, inp, g, rows=None, tokens=None, a_experts=None):
+    """yp on `rows`, y on `tokens` (None: all) against the oracle; the intermediate a on
+    the rows of `a_experts` among them (None: all; its exact reference needs each expert's
+    weights dequantised on the host)."""
     m = moe()
     ids, w = oracle.route(host(inp["logits"]), p.k, p.renormalize)
     keep = oracle.capacity(ids, w, p.E, p.capacity)
@@ -200,19 +212,22 @@ def check_fp8_ffn(p, inp, g, rows=None, tokens=None):
     yp_ref, a_ref, ac, asc = oracle.ffn_rows_fp8(xq, xs, local, *wq, want_a=True,
                                                  nthreads=ORACLE_THREADS)
     # exact gate/up values and the sums of |terms| that bound their accumulation error
-    xd = oracle.dequant(xq, xs, 1)
-    gu = np.empty((2,) + a_ref.shape)
-    su = np.empty((2,) + a_ref.shape)
-    for li in range(experts.size):
-        sel = local == li
+    asel = np.ones(rows.size, bool) if a_experts is None else np.isin(experts[local], a_experts)
+    xd = oracle.dequant(xq[asel], xs[asel], 1)
+    la = local[asel]
+    gu = np.empty((2, int(asel.sum()), p.I))
+    su = np.empty((2, int(asel.sum()), p.I))
+    for li in np.unique(la):
+        sel = la == li
         for j, (cq, cs) in enumerate(wq[:2]):
             wdq = oracle.dequant(cq[li], cs[li], 0)
             gu[j][sel] = xd[sel] @ wdq
             su[j][sel] = np.abs(xd[sel]) @ np.abs(wdq)
-    ridx = torch.as_tensor(rows, device=DEV)
+    ridx = torch.as_tensor(rows[asel], device=DEV)
     codes_g, scales_g = m.split_quantized(p, g["a"])
     check_intermediate(host(codes_g.index_select(0, ridx)), host(scales_g.index_select(0, ridx)),
-                       ac, asc, a_ref, gu[0], gu[1], su[0], su[1])
+                       ac[asel], asc[asel], a_ref[asel], gu[0], gu[1], su[0], su[1], p.H)
+    ridx = torch.as_tensor(rows, device=DEV)
     ok, err, scale = normwise(host(g["yp"].index_select(0, ridx)), yp_ref)
     say(f"  yp: {rows.size} rows, max err {err:.3e} of max|ref| {scale:.3e}")
     assert ok, ("yp", err, scale)
@@ -304,12 +319,31 @@ def test_fp8_full_size_workload(name):
     assert torch.equal(y, g["y"])
     del y
     rng = np.random.default_rng(wl.seed)
-    counts = host(g["counts"])
     offs = host(g["offsets"])
-    last = np.nonzero(counts)[0][-1]
-    # (each sampled token brings k experts whose weights the oracle quantises on the host)
-    tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 2, replace=False)]))
-    rows = np.unique(np.concatenate([rng.choice(N, 8, replace=False), [offs[last + 1] - 1]]))
-    check_fp8_ffn(p, inp, g, rows=rows, tokens=tokens)
+    # The oracle quantises, on the host, the weights of every expert a checked row belongs
+    # to (about 1.4e8 elements a second on 16 threads) and evaluates each row with an
+    # element-wise dequantisation (about 1 s of one thread per DeepSeek-V3 row): every
+    # expert for the two smaller shapes (their 64 random tokens reach nearly all of them
+    # anyway), the experts of 8 tokens for the DeepSeek-V3 shapes (11e9 weight elements in
+    # all).  Checked: the first and the last row of every quantised expert (and, on the
+    # smaller shapes, of every 128-row block inside it), the tokens' rows and their y; the
+    # intermediate a on the rows of 6 of the experts.
+    big = wl.E * 3 * wl.H * wl.I > 4e9
+    tokens = np.unique(np.concatenate([[0, wl.T - 1],
+                                       rng.choice(wl.T, 6 if big else 64, replace=False)]))
+    s2r = host(g["slot_to_row"])
+    need = s2r[tokens].ravel()
+    need = need[need >= 0]
+    experts = (np.unique(np.searchsorted(offs, need, side="right") - 1) if big
+               else np.nonzero(offs[1:] > offs[:-1])[0])
+    rows = []
+    for e in experts:
+        a_, b_ = int(offs[e]), int(offs[e + 1])
+        for r0 in range(a_, b_, b_ - a_ if big else 128):
+            rows += [r0, min(r0 + 128, b_) - 1] if not big else [a_, b_ - 1]
+    rows = np.unique(np.asarray(rows, np.int64))
+    a_experts = rng.choice(experts, min(6, experts.size), replace=False)
+    say(f"  checking {rows.size} rows of {experts.size} experts and {tokens.size} tokens")
+    check_fp8_ffn(p, inp, g, rows=rows, tokens=tokens, a_experts=a_experts)
     del g, inp
     torch.cuda.empty_cache()

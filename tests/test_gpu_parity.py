@@ -124,6 +124,21 @@ def check_ffn_and_combine(p, wl, inp, g, lay, w, rows=None, tokens=None):
         assert np.all(as_f32(host(g["y"][torch.as_tensor(dead, device=DEV)])) == 0.0)
 
 
+def sampled_rows_and_tokens(lay, T, rng, tile=128, n_tokens=64):
+    """Rows and tokens for a full-size check: the first and the last row of every non-empty
+    expert and of every `tile`-row block inside it (the blocks of the grouped GEMM's M tiles,
+    so every work item of the persistent kernels, on whichever XCD range it falls, has rows
+    checked in all its columns), plus n_tokens random tokens (and the first and last)."""
+    offs = lay["offsets"]
+    rows = []
+    for e in range(len(offs) - 1):
+        a, b = int(offs[e]), int(offs[e + 1])
+        for r0 in range(a, b, tile):
+            rows += [r0, min(r0 + tile, b) - 1]
+    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, min(T, n_tokens), replace=False)]))
+    return np.unique(np.asarray(rows, np.int64)), tokens
+
+
 # --------------------------------------------------------------------------------------
 # small problems: every output compared
 # --------------------------------------------------------------------------------------
@@ -143,6 +158,10 @@ SMALL = [
     Workload("f32_cap_ties", T=100, H=64, E=4, k=2, I=32, capacity=30, dtype="f32",
              logits="ties012", seed=17),
     synth.WORKLOADS["tiny_f32"],
+    # many experts on the prefill kernels (T*k > 24 E): expert lookup and XCD ranges over
+    # 600 experts, most with a handful of rows, some empty
+    Workload("prefill_E600", T=2048, H=128, E=600, k=8, I=64, capacity=0, dtype="bf16",
+             logits="normal+bias0.5", seed=18),
 ]
 
 
@@ -320,10 +339,7 @@ def test_full_size_workload(name):
     if wl.T * wl.k * wl.H * wl.I <= 2 ** 31:
         rows, tokens = None, None  # small enough: everything
     else:
-        tokens = np.unique(np.concatenate([[0, wl.T - 1], rng.choice(wl.T, 4, replace=False)]))
-        last = np.nonzero(lay["counts"])[0][-1]
-        rows = np.unique(np.concatenate([rng.choice(N, 8, replace=False),
-                                         [lay["offsets"][last + 1] - 1]]))
+        rows, tokens = sampled_rows_and_tokens(lay, wl.T, rng)
     check_ffn_and_combine(p, wl, inp, g, lay, w, rows=rows, tokens=tokens)
     del g, inp
     torch.cuda.empty_cache()
