@@ -38,7 +38,7 @@ EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_pa
            "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
            "moe_route_grouped", "moe_router", "moe_layer_chunked_workspace_bytes",
            "moe_layer_chunked", "moe_pack_weights_backward", "moe_expert_gate_up_gather_gu",
-           "moe_layer_backward")
+           "moe_layer_backward", "moe_debug_status")
 
 
 class MoeError(RuntimeError):
@@ -67,11 +67,11 @@ class MoeProblem(ctypes.Structure):
                 ("T", "H", "E", "k", "I", "capacity", "renormalize", "act_dtype", "w_dtype")]
 
 
-def _load() -> ctypes.CDLL:
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python expert_ffn_moe_amd/build.py` "
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run `python expert_ffn_moe_amd/build.py` "
                           "(or __graft_entry__.build())")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     PP = ctypes.POINTER(MoeProblem)
     sz = ctypes.c_size_t
@@ -102,6 +102,7 @@ def _load() -> ctypes.CDLL:
                                               ctypes.POINTER(MoeGrads), P, sz, P]),
         "moe_layer_chunked": (ctypes.c_int, [PP, P, P, P, P, ctypes.POINTER(MoeSharedExpert),
                                              ctypes.c_int32, P, P, sz, P, P]),
+        "moe_debug_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -111,6 +112,25 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
+LIB_DEBUG_PATH = os.path.join(_HERE, "libmoe_debug.so")
+_debug_lib = None
+
+
+def debug_lib() -> ctypes.CDLL:
+    """The debug build of the library (device-side precondition checks, moe_debug_status),
+    loaded on first use; same entry points and signatures as `lib`."""
+    global _debug_lib
+    if _debug_lib is None:
+        _debug_lib = _load(LIB_DEBUG_PATH)
+    return _debug_lib
+
+
+def debug_status(dlib=None) -> int:
+    """moe_debug_status of the debug library: the precondition-check bits since the last
+    read (waits for the device)."""
+    v = ctypes.c_uint32(0)
+    _call_on(dlib or debug_lib(), "moe_debug_status", ctypes.byref(v))
+    return int(v.value)
 
 
 def status_str(status: int) -> str:
@@ -202,7 +222,11 @@ def _need(t: torch.Tensor, name: str, shape, dtype):
 
 
 def _call(name: str, *args):
-    st = getattr(lib, name)(*args)
+    _call_on(lib, name, *args)
+
+
+def _call_on(which: ctypes.CDLL, name: str, *args):
+    st = getattr(which, name)(*args)
     if st != MOE_OK:
         raise MoeError(name, st)
 

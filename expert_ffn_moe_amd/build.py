@@ -13,6 +13,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
+# the debug build: MOE_DEBUG_CHECKS makes the kernels check the device-side preconditions
+# (caller-supplied expert ids in [0, E) and distinct within a token) into a status word
+# read by moe_debug_status
+BUILD_DEBUG = os.path.join(HERE, "_build_debug")
+LIB_DEBUG = os.path.join(HERE, "libmoe_debug.so")
 SOURCES = ["moe_api.hip", "route.hip", "dispatch.hip", "combine.hip", "pack.hip", "ffn_bf16.hip",
            "ffn_f32.hip", "quant_fp8.hip", "ffn_fp8.hip", "backward.hip"]
 NO_CONTRACT = {"route.hip", "dispatch.hip"}
@@ -21,9 +26,11 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(BUILD_DEBUG if debug else BUILD, src.replace(".hip", ".o"))
     cmd = [HIPCC, *COMMON]
+    if debug:
+        cmd.append("-DMOE_DEBUG_CHECKS")
     if src in NO_CONTRACT:
         cmd.append("-ffp-contract=off")
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -38,17 +45,19 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Builds libmoe.so (or, with debug, libmoe_debug.so) and returns its path."""
+    out_dir, lib = (BUILD_DEBUG, LIB_DEBUG) if debug else (BUILD, LIB)
+    os.makedirs(out_dir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, debug), SOURCES))
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", lib + ".tmp", *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, debug="--debug" in sys.argv))

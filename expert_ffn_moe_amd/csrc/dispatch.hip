@@ -20,6 +20,21 @@
 namespace moe {
 namespace {
 
+// Whether a routed slot's expert id may index the layout.  Ids are a documented device-side
+// precondition ([0, E), distinct within a token); a build with MOE_DEBUG_CHECKS checks them
+// (launch_check_ids) and treats a slot whose id lies outside [0, E) as dropped, so that an
+// invalid id is reported instead of indexing out of bounds.  (A repeated id stays in bounds:
+// its slots share one row.)
+__device__ __forceinline__ bool id_usable(int e, int E) {
+#ifdef MOE_DEBUG_CHECKS
+  return (unsigned)e < (unsigned)E;
+#else
+  (void)e;
+  (void)E;
+  return true;
+#endif
+}
+
 // Builds, for the chunk of 64 tokens handled by this wavefront, the bitmap
 // bm[e] = {lanes whose token has a (kept) slot routed to e}.  Call from all threads of
 // the block (contains barriers).
@@ -34,7 +49,8 @@ __device__ __forceinline__ void build_chunk_bitmap(uint64_t* bm, const int32_t* 
   if (c < nchunks && t < T) {
     for (int j = 0; j < k; ++j) {
       const size_t s = (size_t)t * k + j;
-      if (!HAS_KEEP || keep[s]) atomicOr((unsigned long long*)&bm[ids[s]], 1ull << lane);
+      if ((!HAS_KEEP || keep[s]) && id_usable(ids[s], E))
+        atomicOr((unsigned long long*)&bm[ids[s]], 1ull << lane);
     }
   }
   __syncthreads();
@@ -132,7 +148,7 @@ __global__ __launch_bounds__(256) void scatter_kernel(
   for (int j = 0; j < k; ++j) {
     const size_t s = (size_t)t * k + j;
     const int e = ids[s];
-    if (!HAS_KEEP || keep[s]) {
+    if ((!HAS_KEEP || keep[s]) && id_usable(e, E)) {
       const int row = s_off[e] + chunk_base[(size_t)c * E + e] + __popcll(bm[e] & below);
       if (CAND) {
         cand_slot[row] = (int32_t)s;
@@ -246,6 +262,27 @@ __global__ __launch_bounds__(1024) void gather_kernel(const uint4* __restrict__ 
 
 inline size_t bitmap_lds(const moe_problem& p) { return (size_t)4 * p.E * sizeof(uint64_t); }
 
+#ifdef MOE_DEBUG_CHECKS
+// Status word of the device-side precondition checks: bit 0 an id outside [0, E), bit 1 an id
+// that appears twice among a token's k slots.  Sticky until read (moe_debug_status).
+__device__ unsigned int g_debug_status;
+
+__global__ __launch_bounds__(256) void check_ids_kernel(const int32_t* __restrict__ ids, int T,
+                                                        int k, int E) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int32_t* r = ids + (size_t)t * k;
+  unsigned int bad = 0;
+  for (int j = 0; j < k; ++j) {
+    const int e = r[j];
+    if (e < 0 || e >= E) bad |= 1u;
+    for (int i = 0; i < j; ++i)
+      if (r[i] == e) bad |= 2u;
+  }
+  if (bad) atomicOr(&g_debug_status, bad);
+}
+#endif
+
 }  // namespace
 
 hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
@@ -316,5 +353,21 @@ hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slo
                        slot_to_row, p.k, nvec, (uint4*)xp);
   return hipGetLastError();
 }
+
+#ifdef MOE_DEBUG_CHECKS
+hipError_t launch_check_ids(const moe_problem& p, const int32_t* ids, hipStream_t s) {
+  hipLaunchKernelGGL(check_ids_kernel, dim3(div_up(p.T, 256)), dim3(256), 0, s, ids, p.T, p.k,
+                     p.E);
+  return hipGetLastError();
+}
+
+hipError_t debug_status_take(uint32_t* out) {
+  hipError_t err = hipDeviceSynchronize();
+  if (err == hipSuccess) err = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_debug_status), 4);
+  const unsigned int zero = 0;
+  if (err == hipSuccess) err = hipMemcpyToSymbol(HIP_SYMBOL(g_debug_status), &zero, 4);
+  return err;
+}
+#endif
 
 }  // namespace moe

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "moe_internal.h"
 
@@ -264,6 +265,39 @@ int check_ws(const moe_problem* p, int op, const void* ws, size_t ws_bytes) {
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
+// ---- aliasing.  A call's outputs (the workspace included) must not overlap its inputs or
+// each other; inputs may share memory.  Byte ranges come from the problem's shapes (row
+// buffers hold T*k rows); NULL or empty ranges overlap nothing.
+struct Span {
+  const void* p;
+  size_t n;
+};
+bool overlap(const Span& a, const Span& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+bool aliased(std::initializer_list<Span> outs, std::initializer_list<Span> ins) {
+  for (auto o = outs.begin(); o != outs.end(); ++o) {
+    for (const Span& i : ins)
+      if (overlap(*o, i)) return true;
+    for (auto o2 = o + 1; o2 != outs.end(); ++o2)
+      if (overlap(*o, *o2)) return true;
+  }
+  return false;
+}
+// Sizes of the shaped buffers of problem p.
+size_t tk_of(const moe_problem& p) { return (size_t)p.T * p.k; }
+size_t act_rows(const moe_problem& p, size_t rows, size_t cols) {
+  return rows * cols * elem_bytes(p.act_dtype);
+}
+size_t a_bytes(const moe_problem& p) {  // the FFN intermediate [T*k, I]
+  return is_fp8(p) ? q_rows_bytes(tk_of(p), p.I) : act_rows(p, tk_of(p), p.I);
+}
+size_t natural_w_bytes(const moe_problem& p) {  // one natural weight set [E, H, I]
+  return (size_t)p.E * p.H * p.I * (p.w_dtype == MOE_F32 ? 4 : 2);
+}
+
 // Capacity after the selection: candidate layout + radix select (no-op without a cap).
 hipError_t run_capacity(const moe_problem& p, int32_t* ids, float* w, uint8_t* keep,
                         const RankScratch& r, hipStream_t s) {
@@ -296,7 +330,12 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
                         const uint8_t* keep, int32_t* counts, int32_t* offsets,
                         int32_t* row_token, int32_t* slot_to_row, void* xp,
                         const RankScratch& r, hipStream_t s) {
-  hipError_t err = launch_chunk_hist(p, ids, keep, r.chunk_hist, s);
+  hipError_t err = hipSuccess;
+#ifdef MOE_DEBUG_CHECKS
+  err = launch_check_ids(p, ids, s);  // the ids may be the caller's
+  if (err != hipSuccess) return err;
+#endif
+  err = launch_chunk_hist(p, ids, keep, r.chunk_hist, s);
   if (err == hipSuccess) err = launch_scan(p, r.chunk_hist, r.chunk_base, counts, s);
   if (err == hipSuccess)
     err = launch_scatter(p, ids, keep, r.chunk_base, counts, offsets, row_token, slot_to_row,
@@ -411,6 +450,13 @@ int moe_pack_weights(const moe_problem* p, const void* w_gate, const void* w_up,
   if (!w_gate || !w_up || !w_down || !packed_gate_up || !packed_down)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(packed_gate_up) || !aligned16(packed_down)) return MOE_ERR_INVALID_ARG;
+  {
+    const size_t nw = natural_w_bytes(*p);
+    if (aliased({{packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_down, moe_packed_bytes(p, MOE_W_DOWN)}},
+                {{w_gate, nw}, {w_up, nw}, {w_down, nw}}))
+      return MOE_ERR_INVALID_ARG;
+  }
   if (p->w_dtype == MOE_FP8)
     return status_of(launch_pack_fp8(*p, w_gate, w_up, w_down, packed_gate_up, packed_down,
                                      as_stream(stream)));
@@ -423,6 +469,10 @@ int moe_route(const moe_problem* p, const float* logits, int32_t* topk_ids, floa
   int st = moe_problem_check(p);
   if (st != MOE_OK) return st;
   if (!logits || !topk_ids || !topk_w || !keep) return MOE_ERR_INVALID_ARG;
+  if (aliased({{topk_ids, tk_of(*p) * 4}, {topk_w, tk_of(*p) * 4}, {keep, tk_of(*p)},
+               {ws, ws_bytes}},
+              {{logits, (size_t)p->T * p->E * 4}}))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   RankScratch r = carve_route(c, *p);
@@ -436,6 +486,10 @@ int moe_route_grouped(const moe_problem* p, const float* logits, int32_t n_group
   int st = moe_problem_check(p);
   if (st != MOE_OK) return st;
   if (!logits || !topk_ids || !topk_w || !keep || !groups_ok(*p, n_group, topk_group))
+    return MOE_ERR_INVALID_ARG;
+  if (aliased({{topk_ids, tk_of(*p) * 4}, {topk_w, tk_of(*p) * 4}, {keep, tk_of(*p)},
+               {ws, ws_bytes}},
+              {{logits, (size_t)p->T * p->E * 4}}))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_ROUTE, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
@@ -454,6 +508,10 @@ int moe_router(const moe_problem* p, const void* x, const void* w_router, int32_
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_INVALID_ARG;
   if (!router_supported(*p)) return MOE_ERR_UNSUPPORTED;
+  if (aliased({{logits, (size_t)p->T * p->E * 4}, {topk_ids, tk_of(*p) * 4},
+               {topk_w, tk_of(*p) * 4}, {keep, tk_of(*p)}, {ws, ws_bytes}},
+              {{x, (size_t)p->T * p->H * 2}, {w_router, (size_t)p->E * p->H * 2}}))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_ROUTER, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   RouterScratch r = carve_router(c, *p);
@@ -473,6 +531,11 @@ int moe_dispatch(const moe_problem* p, const void* x, const int32_t* topk_ids,
   if (!x || !topk_ids || !counts || !offsets || !row_token || !slot_to_row)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || (xp && !aligned16(xp))) return MOE_ERR_INVALID_ARG;
+  if (aliased({{counts, (size_t)p->E * 4}, {offsets, ((size_t)p->E + 1) * 4},
+               {row_token, tk_of(*p) * 4}, {slot_to_row, tk_of(*p) * 4},
+               {xp, act_rows(*p, tk_of(*p), p->H)}, {ws, ws_bytes}},
+              {{x, act_rows(*p, p->T, p->H)}, {topk_ids, tk_of(*p) * 4}, {keep, tk_of(*p)}}))
+    return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_DISPATCH, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   RankScratch r = carve_rank(c, *p, false);
@@ -488,6 +551,10 @@ int moe_expert_gate_up(const moe_problem* p, const void* xp, const int32_t* offs
   if (st != MOE_OK) return st;
   if (!xp || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
   if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
+  if (aliased({{a, a_bytes(*p)}, {is_fp8(*p) ? ws : nullptr, ws_bytes}},
+              {{xp, act_rows(*p, tk_of(*p), p->H)}, {offsets, ((size_t)p->E + 1) * 4},
+               {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)}}))
+    return MOE_ERR_INVALID_ARG;
   FfnScratch f{};
   if (is_fp8(*p)) {  // the quantised input rows live in the workspace
     if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
@@ -507,6 +574,11 @@ int moe_expert_gate_up_gather(const moe_problem* p, const void* x, const int32_t
   if (st != MOE_OK) return st;
   if (!x || !row_token || !offsets || !packed_gate_up || !a) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(packed_gate_up) || !aligned16(a)) return MOE_ERR_INVALID_ARG;
+  if (aliased({{a, a_bytes(*p)}, {is_fp8(*p) ? ws : nullptr, ws_bytes}},
+              {{x, act_rows(*p, p->T, p->H)}, {row_token, tk_of(*p) * 4},
+               {offsets, ((size_t)p->E + 1) * 4},
+               {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)}}))
+    return MOE_ERR_INVALID_ARG;
   FfnScratch f{};
   if (is_fp8(*p)) {
     if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
@@ -528,6 +600,11 @@ int moe_expert_gate_up_gather_gu(const moe_problem* p, const void* x, const int3
   if (!x || !row_token || !offsets || !packed_gate_up || !a || !gu) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(packed_gate_up) || !aligned16(a) || !aligned16(gu))
     return MOE_ERR_INVALID_ARG;
+  if (aliased({{a, a_bytes(*p)}, {gu, tk_of(*p) * 2 * p->I * 2}},
+              {{x, act_rows(*p, p->T, p->H)}, {row_token, tk_of(*p) * 4},
+               {offsets, ((size_t)p->E + 1) * 4},
+               {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)}}))
+    return MOE_ERR_INVALID_ARG;
   return status_of(run_gate_up(*p, x, row_token, offsets, packed_gate_up, a, FfnScratch{},
                                ffn_use_decode(*p), as_stream(stream), gu));
 }
@@ -537,6 +614,9 @@ int moe_quantize_fp8(const void* x, int64_t rows, int32_t cols, uint8_t* codes, 
   if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
   if (rows == 0) return MOE_OK;
   if (!x || !codes || !scales || !aligned16(x) || !aligned16(codes)) return MOE_ERR_INVALID_ARG;
+  if (aliased({{codes, (size_t)rows * cols}, {scales, (size_t)rows * (cols / 32)}},
+              {{x, (size_t)rows * cols * 2}}))
+    return MOE_ERR_INVALID_ARG;
   return status_of(launch_quant_rows(x, rows, cols, nullptr, codes, scales, as_stream(stream)));
 }
 
@@ -547,6 +627,10 @@ int moe_expert_down(const moe_problem* p, const void* a, const int32_t* offsets,
   if (st != MOE_OK) return st;
   if (!a || !offsets || !packed_down || !yp) return MOE_ERR_INVALID_ARG;
   if (!aligned16(a) || !aligned16(packed_down) || !aligned16(yp)) return MOE_ERR_INVALID_ARG;
+  if (aliased({{yp, act_rows(*p, tk_of(*p), p->H)}},
+              {{a, a_bytes(*p)}, {offsets, ((size_t)p->E + 1) * 4},
+               {packed_down, moe_packed_bytes(p, MOE_W_DOWN)}}))
+    return MOE_ERR_INVALID_ARG;
   (void)ws;
   (void)ws_bytes;
   return status_of(
@@ -561,6 +645,11 @@ int moe_expert_ffn(const moe_problem* p, const void* xp, const int32_t* offsets,
   if (!xp || !offsets || !packed_gate_up || !packed_down || !yp) return MOE_ERR_INVALID_ARG;
   if (!aligned16(xp) || !aligned16(packed_gate_up) || !aligned16(packed_down) ||
       !aligned16(yp))
+    return MOE_ERR_INVALID_ARG;
+  if (aliased({{yp, act_rows(*p, tk_of(*p), p->H)}, {ws, ws_bytes}},
+              {{xp, act_rows(*p, tk_of(*p), p->H)}, {offsets, ((size_t)p->E + 1) * 4},
+               {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+               {packed_down, moe_packed_bytes(p, MOE_W_DOWN)}}))
     return MOE_ERR_INVALID_ARG;
   if ((st = check_ws(p, MOE_OP_FFN, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
@@ -579,6 +668,10 @@ int moe_combine(const moe_problem* p, const void* yp, const float* topk_w,
   if (st != MOE_OK) return st;
   if (!yp || !topk_w || !slot_to_row || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(yp) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+  if (aliased({{y, act_rows(*p, p->T, p->H)}},
+              {{yp, act_rows(*p, tk_of(*p), p->H)}, {topk_w, tk_of(*p) * 4},
+               {slot_to_row, tk_of(*p) * 4}}))
+    return MOE_ERR_INVALID_ARG;
   return status_of(launch_combine(*p, yp, topk_w, slot_to_row, nullptr, y, as_stream(stream)));
 }
 
@@ -592,6 +685,16 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   if (!x || !logits || !packed_gate_up || !packed_down || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y) || !aligned16(packed_gate_up) || !aligned16(packed_down))
     return MOE_ERR_INVALID_ARG;
+  {
+    const size_t tk = tk_of(*p);
+    if (aliased({{y, act_rows(*p, p->T, p->H)}, {topk_ids, tk * 4}, {topk_w, tk * 4},
+                 {keep, tk}, {counts, (size_t)p->E * 4}, {offsets, ((size_t)p->E + 1) * 4},
+                 {row_token, tk * 4}, {slot_to_row, tk * 4}, {ws, ws_bytes}},
+                {{x, act_rows(*p, p->T, p->H)}, {logits, (size_t)p->T * p->E * 4},
+                 {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_down, moe_packed_bytes(p, MOE_W_DOWN)}}))
+      return MOE_ERR_INVALID_ARG;
+  }
   if ((st = check_ws(p, MOE_OP_LAYER, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   LayerScratch L = carve_layer(c, *p);
@@ -627,6 +730,13 @@ int moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const vo
   if (!w_gate || !w_up || !w_down || !packed_bwd_gate_up || !packed_bwd_down)
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(packed_bwd_gate_up) || !aligned16(packed_bwd_down)) return MOE_ERR_INVALID_ARG;
+  {
+    const size_t nw = natural_w_bytes(*p);
+    if (aliased({{packed_bwd_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_bwd_down, moe_packed_bytes(p, MOE_W_DOWN)}},
+                {{w_gate, nw}, {w_up, nw}, {w_down, nw}}))
+      return MOE_ERR_INVALID_ARG;
+  }
   return status_of(launch_pack_backward(*p, w_gate, w_up, w_down, packed_bwd_gate_up,
                                         packed_bwd_down, as_stream(stream)));
 }
@@ -653,6 +763,26 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   if (!aligned16(x) || !aligned16(dy) || !aligned16(grads->dx) || (yp && !aligned16(yp)) ||
       (gu && !aligned16(gu)) || (w_router && !aligned16(w_router)))
     return MOE_ERR_INVALID_ARG;
+  {
+    const size_t tk = tk_of(*p), TH2 = (size_t)p->T * p->H * 2;
+    const size_t ew = (size_t)p->E * p->H * p->I * 4;
+    const moe_saved_routing& R = *saved;
+    if (aliased({{grads->dx, TH2}, {grads->dw_gate, ew}, {grads->dw_up, ew},
+                 {grads->dw_down, ew}, {grads->dlogits, (size_t)p->T * p->E * 4},
+                 {grads->dtopk_w, tk * 4},
+                 {w_router ? grads->dw_router : nullptr, (size_t)p->E * p->H * 4},
+                 {ws, ws_bytes}},
+                {{x, TH2}, {logits, (size_t)p->T * p->E * 4},
+                 {w_router, (size_t)p->E * p->H * 2},
+                 {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_down, moe_packed_bytes(p, MOE_W_DOWN)},
+                 {packed_bwd_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_bwd_down, moe_packed_bytes(p, MOE_W_DOWN)}, {R.topk_ids, tk * 4},
+                 {R.topk_w, tk * 4}, {R.offsets, ((size_t)p->E + 1) * 4},
+                 {R.row_token, tk * 4}, {R.slot_to_row, tk * 4}, {yp, tk * p->H * 2},
+                 {gu, tk * 2 * p->I * 2}, {dy, TH2}}))
+      return MOE_ERR_INVALID_ARG;
+  }
   if ((st = check_ws(p, MOE_OP_BACKWARD, ws, ws_bytes)) != MOE_OK) return st;
   Carve c(ws);
   BwdScratch B = carve_backward(c, *p, router_bwd_ok(*p));
@@ -663,6 +793,9 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   const int H = p->H, I = p->I, E = p->E;
   float* dw = grads->dtopk_w ? grads->dtopk_w : B.dw;
   hipError_t err = hipSuccess;
+#ifdef MOE_DEBUG_CHECKS
+  err = launch_check_ids(*p, R.topk_ids, s);  // the saved routing comes from the caller
+#endif
   // the forward's expert outputs, if not saved
   if (!yp) {
     err = run_gate_up(*p, x, R.row_token, R.offsets, packed_gate_up, B.ffn.a, B.ffn, dec, s);
@@ -723,6 +856,16 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   return status_of(err);
 }
 
+int moe_debug_status(uint32_t* status) {
+  if (!status) return MOE_ERR_INVALID_ARG;
+  *status = 0;
+#ifdef MOE_DEBUG_CHECKS
+  return status_of(debug_status_take(status));
+#else
+  return MOE_ERR_UNSUPPORTED;
+#endif
+}
+
 size_t moe_layer_chunked_workspace_bytes(const moe_problem* p, int32_t chunk_tokens,
                                          int32_t shared_I) {
   if (chunked_check(p, chunk_tokens, shared_I) != MOE_OK) return 0;
@@ -744,6 +887,16 @@ int moe_layer_chunked(const moe_problem* p, const void* x, const float* logits,
     return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(y) || !aligned16(packed_gate_up) || !aligned16(packed_down))
     return MOE_ERR_INVALID_ARG;
+  {
+    moe_problem ps = shared_problem(*p, p->T, std::max(shared_I, 1));
+    if (aliased({{y, act_rows(*p, p->T, p->H)}, {ws, ws_bytes}},
+                {{x, act_rows(*p, p->T, p->H)}, {logits, (size_t)p->T * p->E * 4},
+                 {packed_gate_up, moe_packed_bytes(p, MOE_W_GATE_UP)},
+                 {packed_down, moe_packed_bytes(p, MOE_W_DOWN)},
+                 {shared ? shared->packed_gate_up : nullptr, moe_packed_bytes(&ps, MOE_W_GATE_UP)},
+                 {shared ? shared->packed_down : nullptr, moe_packed_bytes(&ps, MOE_W_DOWN)}}))
+      return MOE_ERR_INVALID_ARG;
+  }
   const size_t need = moe_layer_chunked_workspace_bytes(p, chunk_tokens, shared_I);
   if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
   if (((uintptr_t)ws & 255) != 0) return MOE_ERR_INVALID_ARG;

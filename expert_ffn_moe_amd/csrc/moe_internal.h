@@ -82,6 +82,12 @@ hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_
 hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
                                   const int32_t* cand_offsets, const int32_t* cand_slot,
                                   const float* topk_w, uint8_t* keep, hipStream_t s);
+#ifdef MOE_DEBUG_CHECKS
+// Debug builds: checks caller-supplied ids ([0, E), distinct within a token) into the status
+// word; debug_status_take waits for the device, reads the word and clears it.
+hipError_t launch_check_ids(const moe_problem& p, const int32_t* ids, hipStream_t s);
+hipError_t debug_status_take(uint32_t* out);
+#endif
 // Row gather xp[slot_to_row[t, j]] = x[t].
 hipError_t launch_gather(const moe_problem& p, const void* x, const int32_t* slot_to_row,
                          void* xp, hipStream_t s);

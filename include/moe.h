@@ -35,14 +35,21 @@
  *     yp) hold T*k rows: the number of kept assignments N is only known on the device.
  *   - Errors are reported synchronously, before anything is enqueued:
  *       MOE_ERR_INVALID_ARG  NULL required pointer, non-positive sizes, k > E, unknown
- *                            dtype, misaligned pointer;
+ *                            dtype, misaligned pointer, or aliasing: an output buffer (the
+ *                            workspace included) whose byte range, sized from the problem as
+ *                            documented for each call (row buffers hold T*k rows), overlaps
+ *                            an input buffer or another output (inputs may share memory);
  *       MOE_ERR_UNSUPPORTED  a valid problem the kernels do not handle (see
  *                            moe_problem_check);
  *       MOE_ERR_WORKSPACE    ws_bytes < moe_workspace_bytes(p, op);
  *       MOE_ERR_HIP          a launch failed (hipGetLastError after enqueueing).
  *     No call ever falls back to another implementation.
- *   - Device-side preconditions (not checked): logits finite; caller-supplied ids in
- *     [0, E) and distinct within a token; input and output buffers do not overlap.
+ *   - Device-side preconditions (not checked in the release library): logits finite;
+ *     caller-supplied ids in [0, E) and distinct within a token.  The debug library
+ *     (libmoe_debug.so, built with MOE_DEBUG_CHECKS) checks the ids wherever a call takes
+ *     them from the caller (moe_dispatch, moe_layer_backward), treats a slot whose id lies
+ *     outside [0, E) as dropped instead of indexing with it, and reports violations through
+ *     moe_debug_status.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -100,6 +107,14 @@ typedef enum { MOE_W_GATE_UP = 0, MOE_W_DOWN = 1 } moe_weight_set;
 
 /* Text for a status code (static storage). */
 const char* moe_status_str(int status);
+
+/* Debug library only ([axolotl] `validate_expert_parallel_topology`: what the kernels cannot
+ * handle is reported, never run another way): waits for the current device, writes the
+ * sticky status word of its precondition checks to *status and clears it.  Bit 0: an expert
+ * id outside [0, E) was passed; bit 1: a token's k ids were not distinct.  The release
+ * library sets *status = 0 and returns MOE_ERR_UNSUPPORTED; MOE_ERR_INVALID_ARG if status
+ * is NULL. */
+int moe_debug_status(uint32_t* status);
 
 /* Host-only validation of a problem ([axolotl] `validate_expert_parallel_topology`:
  * layouts the kernels do not handle are rejected up front, never run another way).

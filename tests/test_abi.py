@@ -17,6 +17,13 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
 
 
+def fake_ptrs(n, base=1 << 44):
+    """n distinct 256-aligned host-side stand-ins for device pointers, 64 GiB apart (so no
+    two of the buffers a call sizes from its problem overlap).  Only calls that return before
+    launching anything may receive them."""
+    return [ctypes.c_void_p(base + (i << 36)) for i in range(n)]
+
+
 @pytest.fixture(scope="module")
 def moe():
     import expert_ffn_moe_amd
@@ -91,16 +98,16 @@ def test_calls_reject_bad_arguments_before_touching_the_device(moe):
     c = p.c()
     st = moe.lib.moe_route(ctypes.byref(c), None, None, None, None, None, 0, None)
     assert st == moe.MOE_ERR_INVALID_ARG
-    fake = ctypes.c_void_p(256)
-    st = moe.lib.moe_route(ctypes.byref(c), fake, fake, fake, fake, None, 0, None)
+    f = fake_ptrs(6)
+    st = moe.lib.moe_route(ctypes.byref(c), f[0], f[1], f[2], f[3], None, 0, None)
     assert st == moe.MOE_ERR_WORKSPACE
-    st = moe.lib.moe_combine(ctypes.byref(c), ctypes.c_void_p(8), fake, fake, fake, None)
+    st = moe.lib.moe_combine(ctypes.byref(c), ctypes.c_void_p(8), f[1], f[2], f[3], None)
     assert st == moe.MOE_ERR_INVALID_ARG  # misaligned yp
-    st = moe.lib.moe_expert_gate_up_gather(ctypes.byref(c), fake, None, fake, fake, fake, None, 0,
+    st = moe.lib.moe_expert_gate_up_gather(ctypes.byref(c), f[0], None, f[1], f[2], f[3], None, 0,
                                            None)
     assert st == moe.MOE_ERR_INVALID_ARG  # gather without row_token
     bad = moe.Problem(T=64, H=100, E=8, k=2, I=128).c()
-    st = moe.lib.moe_layer(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, None, None,
+    st = moe.lib.moe_layer(ctypes.byref(bad), f[0], f[1], f[2], f[3], f[4], None, None, None, None,
                            None, None, None, None, 0, None)
     assert st == moe.MOE_ERR_UNSUPPORTED
 
@@ -153,18 +160,61 @@ def test_router_workspace_holds_the_partial_logits(moe):
 
 
 def test_router_and_grouped_route_reject_bad_arguments(moe):
-    fake = ctypes.c_void_p(256)
+    lg, ids, w, keep, x, wr = fake_ptrs(6)
     p = moe.Problem(T=64, H=128, E=64, k=4, I=128).c()
     P = ctypes.byref(p)
     gr = moe.lib.moe_route_grouped
-    assert gr(P, fake, 3, 1, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 64 % 3
-    assert gr(P, fake, 8, 9, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 9 > 8
-    assert gr(P, fake, 64, 2, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # k > 2
-    assert gr(P, fake, 128, 1, fake, fake, fake, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert gr(P, lg, 3, 1, ids, w, keep, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 64 % 3
+    assert gr(P, lg, 8, 9, ids, w, keep, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # 9 > 8
+    assert gr(P, lg, 64, 2, ids, w, keep, None, 0, None) == moe.MOE_ERR_INVALID_ARG  # k > 2
+    assert gr(P, lg, 128, 1, ids, w, keep, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     r = moe.lib.moe_router
-    assert r(P, fake, fake, 1, 1, None, fake, fake, fake, None, 0, None) == moe.MOE_ERR_WORKSPACE
-    assert r(P, ctypes.c_void_p(8), fake, 1, 1, None, fake, fake, fake, None, 0,
+    assert r(P, x, wr, 1, 1, None, ids, w, keep, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert r(P, ctypes.c_void_p(8), wr, 1, 1, None, ids, w, keep, None, 0,
              None) == moe.MOE_ERR_INVALID_ARG
     f32 = moe.Problem(T=64, H=128, E=64, k=4, I=128, dtype="f32").c()
-    assert r(ctypes.byref(f32), fake, fake, 1, 1, None, fake, fake, fake, None, 0,
+    assert r(ctypes.byref(f32), x, wr, 1, 1, None, ids, w, keep, None, 0,
              None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_overlapping_buffers_are_rejected(moe):
+    """An output overlapping an input, another output or the workspace is refused on the
+    host (MOE_ERR_INVALID_ARG) before anything is enqueued; buffers that only touch are
+    not overlapping.  With distinct buffers the calls below go on to their next host check
+    (the missing workspace)."""
+    INV, WS = moe.MOE_ERR_INVALID_ARG, moe.MOE_ERR_WORKSPACE
+    T, H, E, k, I = 64, 128, 8, 2, 128
+    c = moe.Problem(T=T, H=H, E=E, k=k, I=I, capacity=4).c()
+    P = ctypes.byref(c)
+    lg, ids, w, keep, x, xp, cnt, off, rt, s2r, ws = fake_ptrs(11)
+    at = lambda ptr, nbytes: ctypes.c_void_p(ptr.value + nbytes)
+    route = moe.lib.moe_route
+    assert route(P, lg, ids, w, keep, None, 0, None) == WS
+    assert route(P, lg, at(lg, 64), w, keep, None, 0, None) == INV        # ids inside logits
+    assert route(P, lg, ids, at(ids, T * k * 4 - 4), keep, None, 0, None) == INV  # w over ids' end
+    assert route(P, lg, ids, at(ids, T * k * 4), keep, None, 0, None) == WS  # w right after ids
+    assert route(P, lg, ids, w, keep, at(keep, 8), 1 << 20, None) == INV  # workspace over keep
+    disp = moe.lib.moe_dispatch
+    args = lambda **kw: [kw.get(n, v) for n, v in (("x", x), ("ids", ids), ("keep", keep),
+                                                     ("cnt", cnt), ("off", off), ("rt", rt),
+                                                     ("s2r", s2r), ("xp", xp))]
+    ok = args()
+    assert disp(P, *ok, None, 0, None) == WS
+    assert disp(P, *args(xp=at(x, 16 * H * 2)), None, 0, None) == INV    # xp over x
+    assert disp(P, *args(s2r=rt), None, 0, None) == INV                   # two outputs alike
+    assert disp(P, *args(off=at(ids, 4)), None, 0, None) == INV           # offsets over ids
+    # inputs may share memory (keep inside the ids buffer is only read)
+    assert disp(P, *args(keep=at(ids, 8)), None, 0, None) == WS
+    # calls without a workspace check: only the refusals can be exercised off the GPU
+    import torch
+    buf = torch.empty(4 << 20, dtype=torch.uint8)  # host bytes; nothing is launched
+    yp, y = buf[: T * k * H * 2], buf[T * H * 2:]  # aliased views: y starts inside yp
+    assert moe.lib.moe_combine(P, ctypes.c_void_p(yp.data_ptr()), w, s2r,
+                               ctypes.c_void_p(y.data_ptr()), None) == INV
+    pb = moe.Problem(T=T, H=H, E=E, k=k, I=I).c()
+    PB = ctypes.byref(pb)
+    assert moe.lib.moe_expert_down(PB, xp, off, x, at(xp, 256), None, 0, None) == INV  # yp over a
+    assert moe.lib.moe_layer(PB, x, lg, keep, cnt, at(x, 512), None, None, None, None, None,
+                             None, None, ws, 1 << 30, None) == INV        # y over x
+    assert moe.lib.moe_layer(PB, x, lg, keep, cnt, xp, ids, at(ids, 4), None, None, None,
+                             None, None, ws, 1 << 30, None) == INV        # topk_w over topk_ids
