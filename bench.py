@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer tokens/sec on 1 MI355X; % bf16 MFMA peak (GEMM), % HBM peak (dispatch)"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, GB/s
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "f32": 157.3}  # dense MFMA bf16, fp8; fp32 vector
-DEFAULT_WORKLOAD = "qwen3_30b_a3b"
+DEFAULT_WORKLOAD = "dsv3_prefill"  # the largest single-GPU workload
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -41,9 +41,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU reaches its steady clock only after some 50-100 ms of back-to-back steps (a
-    # 0.46 ms step runs at ~0.50 ms over the first 20): the defaults warm up for 200 steps
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    # 0.46 ms step runs at ~0.50 ms over the first 20): the warm-up runs at least
+    # --warmup steps and at least --warmup-seconds of them, whichever is longer
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5)
     ap.add_argument("--config", default=DEFAULT_WORKLOAD)
     ap.add_argument("--router", action="store_true",
                     help="route from the hidden states: router GEMM x W_r^T + selection "
@@ -142,7 +144,12 @@ def cpu_baseline(wl, inp, target_s, wr=None, groups=(1, 1)):
 
     import torch
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    # every core this process may use, capped by the thread count the environment sets
+    # (OMP_NUM_THREADS: a host shared between GPUs gives each its share)
+    avail = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(avail, int(env)) if env.isdigit() and int(env) > 0 else avail
+    model, ncpu = host_cpu()
     host = {n: (synth.bf16_bits(t) if t.dtype == torch.bfloat16 else t.cpu().numpy())
             for n, t in inp.items()}
     fp8 = wl.dtype == "fp8"
@@ -185,8 +192,38 @@ def cpu_baseline(wl, inp, target_s, wr=None, groups=(1, 1)):
     t_ffn = ffn_for(tokens)
     total = t_route + t_ffn * wl.T / n
     return dict(value=round(wl.T / total, 2), unit="tokens/s", cores=threads, kind="oracle",
+                cpu_model=model, host_logical_cpus=ncpu, affinity_cpus=avail,
                 sample=f"routing+capacity+layout over all {wl.T} tokens ({t_route:.2f} s); FFN+combine "
                        f"over {n} random tokens ({t_ffn:.2f} s), scaled to {wl.T} tokens")
+
+
+def warm_up(fn, min_steps, min_seconds):
+    """Runs fn at least min_steps times and for at least min_seconds of wall time (the GPU
+    clock settles only after some 50-100 ms of back-to-back work); returns the count."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_steps or time.perf_counter() - t0 < min_seconds:
+        fn()
+        n += 1
+        if n % 8 == 0 or n >= min_steps:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return n
+
+
+def host_cpu():
+    """CPU model and logical CPU count of the host, from /proc/cpuinfo."""
+    model, n = "unknown", 0
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                model = ln.split(":", 1)[1].strip()
+                n += 1
+    except OSError:
+        pass
+    return model, n
 
 
 def time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev):
@@ -356,9 +393,7 @@ def main():
         moe.combine(p, yp, w, disp["slot_to_row"], out=y)
         mark(5)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_steps = warm_up(step, args.warmup, args.warmup_seconds)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -444,7 +479,8 @@ def main():
         layer_calls = time_layer_calls(args, moe, p, wl, inp, pgu, pd, dev)
     out = {
         "metric": METRIC, "value": round(wl.T / sec, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(sec * 1e3, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_steps,
+        "ms_per_step": round(sec * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded; routing logits and weights drawn per the workload recipe)",
         "config": {"workload": wl.name + ("+router" if args.router else ""), "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,
