@@ -38,7 +38,8 @@ EXPORTS = ("moe_status_str", "moe_problem_check", "moe_workspace_bytes", "moe_pa
            "moe_expert_down", "moe_combine", "moe_layer", "moe_quantize_fp8",
            "moe_route_grouped", "moe_router", "moe_layer_chunked_workspace_bytes",
            "moe_layer_chunked", "moe_pack_weights_backward", "moe_expert_gate_up_gather_gu",
-           "moe_layer_backward", "moe_debug_status")
+           "moe_layer_backward", "moe_debug_status", "moe_layer_static",
+           "moe_layer_static_max_bytes")
 
 
 class MoeError(RuntimeError):
@@ -103,6 +104,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
         "moe_layer_chunked": (ctypes.c_int, [PP, P, P, P, P, ctypes.POINTER(MoeSharedExpert),
                                              ctypes.c_int32, P, P, sz, P, P]),
         "moe_debug_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32)]),
+        "moe_layer_static": (ctypes.c_int, [PP, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "moe_layer_static_max_bytes": (ctypes.c_size_t, []),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)

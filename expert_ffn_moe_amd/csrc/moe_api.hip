@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_internal.h"
 
@@ -383,6 +384,29 @@ hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
   return launch_down_bf16(p, a, offsets, pd, yp, decode, s);
 }
 
+// ---- the no-allocation layer (moe_layer_static): moe_layer's workspace in a file-scope
+// device array, its address looked up once per device (the array's name is only a host-side
+// stand-in: kernels must be given the device address).
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (NULL on failure).
+void* static_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -719,6 +743,24 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
     err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, ffn_use_decode(*p), s);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, nullptr, y, s);
   return status_of(err);
+}
+
+size_t moe_layer_static_max_bytes(void) { return kStaticScratchBytes; }
+
+int moe_layer_static(const moe_problem* p, const void* x, const float* logits,
+                     const void* packed_gate_up, const void* packed_down, void* y,
+                     int32_t* topk_ids, float* topk_w, uint8_t* keep, int32_t* counts,
+                     int32_t* offsets, int32_t* row_token, int32_t* slot_to_row, void* stream) {
+  int st = moe_problem_check(p);
+  if (st != MOE_OK) return st;
+  const size_t need = ws_bytes_of(*p, MOE_OP_LAYER);
+  if (need > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = static_scratch();
+  if (!ws) return MOE_ERR_HIP;
+  // every kernel of the layer writes what it later reads: nothing in the scratch needs
+  // clearing between calls
+  return moe_layer(p, x, logits, packed_gate_up, packed_down, y, topk_ids, topk_w, keep, counts,
+                   offsets, row_token, slot_to_row, ws, kStaticScratchBytes, stream);
 }
 
 int moe_pack_weights_backward(const moe_problem* p, const void* w_gate, const void* w_up,

@@ -305,6 +305,25 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
               size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------
+ * moe_layer_static -- moe_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation): the same
+ * arguments without a workspace; the workspace is a device array inside the library of
+ * moe_layer_static_max_bytes() bytes (32 MiB), one per GPU the library runs on, held until
+ * the process ends.  Nothing is allocated or freed by the call.  Every call on a GPU shares
+ * that GPU's array, which keeps the last call's contents (the layer writes everything it
+ * later reads, so nothing needs clearing): calls that overlap in time on one GPU (other
+ * streams, other host threads) race and give undefined results.  MOE_ERR_WORKSPACE if
+ * moe_workspace_bytes(p, MOE_OP_LAYER) exceeds the array (e.g. decode batches of a few
+ * hundred tokens fit at DeepSeek-V3 width); otherwise errors and results as moe_layer,
+ * bit for bit.
+ * --------------------------------------------------------------------------------- */
+size_t moe_layer_static_max_bytes(void);
+int moe_layer_static(const moe_problem* p, const void* x, const float* logits,
+                     const void* packed_gate_up, const void* packed_down, void* y,
+                     int32_t* topk_ids, float* topk_w, uint8_t* keep, int32_t* counts,
+                     int32_t* offsets, int32_t* row_token, int32_t* slot_to_row, void* stream);
+
+/* ---------------------------------------------------------------------------------
  * moe_layer_chunked -- moe_layer over chunks of tokens, with the next chunk's layout
  * built on a second stream while the current chunk's experts run, and an optional shared
  * expert ([LightLLM] PR body: the chunked expanded forward bounds each call's temporary
