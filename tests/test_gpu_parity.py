@@ -158,6 +158,10 @@ SMALL = [
     Workload("f32_cap_ties", T=100, H=64, E=4, k=2, I=32, capacity=30, dtype="f32",
              logits="ties012", seed=17),
     synth.WORKLOADS["tiny_f32"],
+    # over 384 rows per expert: the down projection on the 256 x 256 tile, several M tiles
+    # per expert with ragged tails, a partial N tile (H = 320: 10 panels)
+    Workload("prefill_wide_tile", T=2000, H=320, E=4, k=2, I=192, capacity=0, dtype="bf16",
+             logits="normal+bias0.5", seed=19),
     # many experts on the prefill kernels (T*k > 24 E): expert lookup and XCD ranges over
     # 600 experts, most with a handful of rows, some empty
     Workload("prefill_E600", T=2048, H=128, E=600, k=8, I=64, capacity=0, dtype="bf16",
