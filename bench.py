@@ -1,23 +1,25 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic tokens, the kernel
-sequence of moe_layer issued through the staged entry points so that every stage can be
-timed:
-  moe_route -> moe_dispatch (layout only) -> moe_expert_gate_up_gather -> moe_expert_down
-  -> moe_combine
-(capacity selection runs inside moe_route when the workload has a cap; gate/up reads the
-token rows through row_token, so no permuted copy of x is written).  Inputs and the packed
-expert weights are resident in HBM before timing starts.
+One step = one pass of the whole path over one batch of synthetic tokens: one moe_layer
+call (routing with the layout's chunk histogram in the same launch, the layout, gate/up
+reading the token rows through row_token, down, combine; the capacity selection too when
+the workload has a cap).  With --router the step is the staged sequence below with
+moe_router in front.  Inputs and the packed expert weights are resident in HBM before
+timing starts.
 
 Prints one JSON line: whole-step throughput in tokens/s, the roofline of the dominant
 kernel (per-launch algorithmic bytes or flops over its HIP-event-timed duration on the
 launch stream), and the CPU oracle timed on a bounded sample of the same workload.
 
-Two passes over the same steps: the timed pass (the `value`) records no events between the
-stages -- a timing event between kernels costs about 10 us of GPU time on this stack --
-and a second pass of the same number of steps records an event before and after every
-stage, on the launch stream, for the per-stage durations and the dominant kernel's
-roofline.
+Two passes over the same steps: the timed pass (the `value`) records no events -- a timing
+event between kernels costs about 10 us of GPU time on this stack -- and a second pass of
+the same number of steps issues the layer's kernel sequence through the staged entry
+points,
+  moe_route -> moe_dispatch (layout only) -> moe_expert_gate_up_gather -> moe_expert_down
+  -> moe_combine,
+with an event before and after every stage, on the launch stream, for the per-stage
+durations and the dominant kernel's roofline.  (There the layout counts its chunk
+histogram in a launch of its own: moe_route hands none over.)
 """
 import argparse
 import hashlib
@@ -393,10 +395,19 @@ def main():
         moe.combine(p, yp, w, disp["slot_to_row"], out=y)
         mark(5)
 
-    warm_steps = warm_up(step, args.warmup, args.warmup_seconds)
+    layer_ws = None if wr is not None else moe.workspace(p, moe.OP_LAYER, dev)
+
+    def layer_step():
+        if layer_ws is None:
+            step()
+        else:
+            moe.layer(p, inp["x"], inp["logits"], pgu, pd, out=y, ws=layer_ws)
+
+    warm_up(step, 2, 0.0)  # the stage pass's calls
+    warm_steps = warm_up(layer_step, args.warmup, args.warmup_seconds)
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        layer_step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     sec = (t1 - t0) / args.steps
@@ -481,6 +492,7 @@ def main():
         "metric": METRIC, "value": round(wl.T / sec, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warm_steps,
         "ms_per_step": round(sec * 1e3, 4),
+        "step_call": "moe_layer" if layer_ws is not None else "staged (moe_router first)",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
         "data": "synthetic (seeded; routing logits and weights drawn per the workload recipe)",
         "config": {"workload": wl.name + ("+router" if args.router else ""), "T": wl.T, "H": wl.H, "E": wl.E, "k": wl.k, "I": wl.I,

@@ -35,6 +35,24 @@ __device__ __forceinline__ bool id_usable(int e, int E) {
 #endif
 }
 
+// Chunks (wavefronts) per block of the histogram and scatter launches: one, so that the
+// scattered row stores of a layout spread over as many CUs as it has chunks.
+constexpr int kLayoutWaves = 1;
+
+// Slots are read in batches of kBatch (all loads issued before the first use: the LDS
+// atomics that consume them would otherwise wait for each load in turn).
+constexpr int kBatch = 8;
+
+// The expert id of slot s if the slot exists and is kept, else -1 (the id and the keep flag
+// are loaded independently, so that neither waits for the other).
+template <bool HAS_KEEP>
+__device__ __forceinline__ int load_slot(const int32_t* __restrict__ ids,
+                                         const uint8_t* __restrict__ keep, size_t s, bool exists) {
+  if (!exists) return -1;
+  const int e = ids[s];
+  return (!HAS_KEEP || keep[s]) ? e : -1;
+}
+
 // Builds, for the chunk of 64 tokens handled by this wavefront, the bitmap
 // bm[e] = {lanes whose token has a (kept) slot routed to e}.  Call from all threads of
 // the block (contains barriers).
@@ -47,23 +65,30 @@ __device__ __forceinline__ void build_chunk_bitmap(uint64_t* bm, const int32_t* 
   __syncthreads();
   const int t = c * kChunk + lane;
   if (c < nchunks && t < T) {
-    for (int j = 0; j < k; ++j) {
-      const size_t s = (size_t)t * k + j;
-      if ((!HAS_KEEP || keep[s]) && id_usable(ids[s], E))
-        atomicOr((unsigned long long*)&bm[ids[s]], 1ull << lane);
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      int ev[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const size_t s = (size_t)t * k + j0 + j;
+        ev[j] = load_slot<HAS_KEEP>(ids, keep, s, j0 + j < k);
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (ev[j] != -1 && id_usable(ev[j], E))
+          atomicOr((unsigned long long*)&bm[ev[j]], 1ull << lane);
     }
   }
   __syncthreads();
 }
 
 template <bool HAS_KEEP>
-__global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restrict__ ids,
+__global__ __launch_bounds__(64 * kLayoutWaves) void chunk_hist_kernel(const int32_t* __restrict__ ids,
                                                          const uint8_t* __restrict__ keep, int T,
                                                          int E, int k, int nchunks,
                                                          int32_t* __restrict__ chunk_hist) {
   extern __shared__ uint64_t smem_bm[];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + wave;
+  const int c = blockIdx.x * kLayoutWaves + wave;
   uint64_t* bm = smem_bm + (size_t)wave * E;
   build_chunk_bitmap<HAS_KEEP>(bm, ids, keep, T, E, k, c, nchunks);
   if (c < nchunks)
@@ -81,13 +106,16 @@ __global__ __launch_bounds__(1024) void scan_cols_kernel(const int32_t* __restri
   const int per = div_up(nchunks, 16);
   const int c0 = min(nchunks, wave * per), c1 = min(nchunks, c0 + per);
   int sum = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) sum += chunk_hist[(size_t)c * E + e];
+  }
   part[wave][lane] = sum;
   __syncthreads();
   int base = 0;
   for (int w = 0; w < wave; ++w) base += part[w][lane];
   if (e < E) {
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) {
       const int v = chunk_hist[(size_t)c * E + e];
       chunk_base[(size_t)c * E + e] = base;
@@ -97,16 +125,17 @@ __global__ __launch_bounds__(1024) void scan_cols_kernel(const int32_t* __restri
   }
 }
 
-// Exclusive scan of counts[0..E) into s_off[0..E] (E <= kMaxE = 1024), by a block of 256
-// threads (4 experts per thread).  Contains barriers: call from every thread of the block.
+// Exclusive scan of counts[0..E) into s_off[0..E] by a block of WAVES wavefronts, PER experts
+// per thread (E <= 64 WAVES PER).  Contains barriers: call from every thread of the block.
+template <int WAVES, int PER>
 __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts, int E,
                                               int* s_off) {
-  __shared__ int wsum[4];
+  __shared__ int wsum[WAVES];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int v[4], sum = 0;
+  int v[PER], sum = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
     v[i] = e < E ? counts[e] : 0;
     sum += v[i];
   }
@@ -116,50 +145,79 @@ __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts
   int base = inc - sum;
   for (int w = 0; w < wave; ++w) base += wsum[w];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = tid * 4 + i;
+  for (int i = 0; i < PER; ++i) {
+    const int e = tid * PER + i;
     if (e < E) s_off[e] = base;
     base += v[i];
   }
-  if (tid == 255) s_off[E] = base;  // the last thread ends with the total
+  if (tid == 64 * WAVES - 1) s_off[E] = base;  // the last thread ends with the total
   __syncthreads();
+}
+
+// Rows of the (kept) slots of the chunk this wavefront handles: row = offsets[e] + chunk
+// base of e + the rank of the token among the chunk's tokens routed to e (bitmap popcount).
+// base(e): the number of rows of e in the chunks before this one.
+template <bool HAS_KEEP, bool CAND, class Base>
+__device__ __forceinline__ void scatter_chunk(const uint64_t* bm, const int* s_off, Base base,
+                                              const int32_t* __restrict__ ids,
+                                              const uint8_t* __restrict__ keep, int T, int E,
+                                              int k, int c, int nchunks,
+                                              int32_t* __restrict__ row_token,
+                                              int32_t* __restrict__ slot_to_row,
+                                              int32_t* __restrict__ cand_slot) {
+  const int lane = threadIdx.x & 63;
+  const int t = c * kChunk + lane;
+  if (c >= nchunks || t >= T) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int j0 = 0; j0 < k; j0 += kBatch) {
+    int ev[kBatch], bv[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const size_t s = (size_t)t * k + j0 + j;
+      ev[j] = load_slot<HAS_KEEP>(ids, keep, s, j0 + j < k);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) bv[j] = (ev[j] != -1 && id_usable(ev[j], E)) ? base(ev[j]) : 0;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (j0 + j >= k) break;
+      const size_t s = (size_t)t * k + j0 + j;
+      const int e = ev[j];
+      if (e != -1 && id_usable(e, E)) {
+        const int row = s_off[e] + bv[j] + __popcll(bm[e] & below);
+        if (CAND) {
+          cand_slot[row] = (int32_t)s;
+        } else {
+          row_token[row] = t;
+          slot_to_row[s] = row;
+        }
+      } else if (!CAND) {
+        slot_to_row[s] = -1;
+      }
+    }
+  }
 }
 
 // Every block scans the counts into offsets itself (E <= 1024 values, cheaper than a
 // launch of its own); block 0 also writes them out.
 template <bool HAS_KEEP, bool CAND>
-__global__ __launch_bounds__(256) void scatter_kernel(
+__global__ __launch_bounds__(64 * kLayoutWaves) void scatter_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ keep, int T, int E, int k,
     int nchunks, const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token,
     int32_t* __restrict__ slot_to_row, int32_t* __restrict__ cand_slot) {
   extern __shared__ uint64_t smem_bm[];
   __shared__ int s_off[kMaxE + 4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int c = blockIdx.x * 4 + wave;
-  block_offsets(counts, E, s_off);
+  const int wave = threadIdx.x >> 6;
+  const int c = blockIdx.x * kLayoutWaves + wave;
+  block_offsets<kLayoutWaves, kMaxE / (64 * kLayoutWaves)>(counts, E, s_off);
   if (blockIdx.x == 0)
     for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
   uint64_t* bm = smem_bm + (size_t)wave * E;
   build_chunk_bitmap<HAS_KEEP>(bm, ids, keep, T, E, k, c, nchunks);
-  const int t = c * kChunk + lane;
-  if (c >= nchunks || t >= T) return;
-  const uint64_t below = (1ull << lane) - 1ull;
-  for (int j = 0; j < k; ++j) {
-    const size_t s = (size_t)t * k + j;
-    const int e = ids[s];
-    if ((!HAS_KEEP || keep[s]) && id_usable(e, E)) {
-      const int row = s_off[e] + chunk_base[(size_t)c * E + e] + __popcll(bm[e] & below);
-      if (CAND) {
-        cand_slot[row] = (int32_t)s;
-      } else {
-        row_token[row] = t;
-        slot_to_row[s] = row;
-      }
-    } else if (!CAND) {
-      slot_to_row[s] = -1;
-    }
-  }
+  const int32_t* cb = chunk_base + (size_t)c * E;
+  scatter_chunk<HAS_KEEP, CAND>(bm, s_off, [cb](int e) { return cb[e]; }, ids, keep, T, E, k,
+                                c, nchunks, row_token, slot_to_row, cand_slot);
 }
 
 // Capacity selection, one block per expert.  Keys (weight bits << 32) | (~token) are
@@ -260,7 +318,9 @@ __global__ __launch_bounds__(1024) void gather_kernel(const uint4* __restrict__ 
   }
 }
 
-inline size_t bitmap_lds(const moe_problem& p) { return (size_t)4 * p.E * sizeof(uint64_t); }
+inline size_t bitmap_lds(const moe_problem& p) {
+  return (size_t)kLayoutWaves * p.E * sizeof(uint64_t);
+}
 
 #ifdef MOE_DEBUG_CHECKS
 // Status word of the device-side precondition checks: bit 0 an id outside [0, E), bit 1 an id
@@ -285,47 +345,42 @@ __global__ __launch_bounds__(256) void check_ids_kernel(const int32_t* __restric
 
 }  // namespace
 
-hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                             int32_t* chunk_hist, hipStream_t s) {
+static hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids,
+                                    const uint8_t* keep, int32_t* chunk_hist, hipStream_t s) {
   const int nchunks = div_up(p.T, kChunk);
-  dim3 grid(div_up(nchunks, 4));
+  dim3 grid(div_up(nchunks, kLayoutWaves));
   if (keep)
-    hipLaunchKernelGGL(chunk_hist_kernel<true>, grid, dim3(256), bitmap_lds(p), s, ids, keep,
-                       p.T, p.E, p.k, nchunks, chunk_hist);
+    hipLaunchKernelGGL(chunk_hist_kernel<true>, grid, dim3(64 * kLayoutWaves), bitmap_lds(p), s,
+                       ids, keep, p.T, p.E, p.k, nchunks, chunk_hist);
   else
-    hipLaunchKernelGGL(chunk_hist_kernel<false>, grid, dim3(256), bitmap_lds(p), s, ids, keep,
-                       p.T, p.E, p.k, nchunks, chunk_hist);
+    hipLaunchKernelGGL(chunk_hist_kernel<false>, grid, dim3(64 * kLayoutWaves), bitmap_lds(p), s,
+                       ids, keep, p.T, p.E, p.k, nchunks, chunk_hist);
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
-                       int32_t* counts, hipStream_t s) {
+hipError_t launch_layout(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                         int32_t* chunk_hist, int32_t* chunk_base, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* slot_to_row,
+                         int32_t* cand_slot, hipStream_t s) {
   const int nchunks = div_up(p.T, kChunk);
-  hipLaunchKernelGGL(scan_cols_kernel, dim3(div_up(p.E, 64)), dim3(1024), 0, s, chunk_hist,
-                     p.E, nchunks, chunk_base, counts);
-  return hipGetLastError();
-}
-
-hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                          const int32_t* chunk_base, const int32_t* counts, int32_t* offsets,
-                          int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
-                          hipStream_t s) {
-  const int nchunks = div_up(p.T, kChunk);
-  dim3 grid(div_up(nchunks, 4));
+  hipError_t err = launch_chunk_hist(p, ids, keep, chunk_hist, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(scan_cols_kernel, dim3(div_up(p.E, 64)), dim3(1024), 0, s, chunk_hist, p.E,
+                     nchunks, chunk_base, counts);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  dim3 grid(div_up(nchunks, kLayoutWaves));
   const size_t lds = bitmap_lds(p);
-  if (cand_slot) {
-    hipLaunchKernelGGL((scatter_kernel<false, true>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
-                       slot_to_row, cand_slot);
-  } else if (keep) {
-    hipLaunchKernelGGL((scatter_kernel<true, false>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
-                       slot_to_row, cand_slot);
-  } else {
-    hipLaunchKernelGGL((scatter_kernel<false, false>), grid, dim3(256), lds, s, ids, keep, p.T,
-                       p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,
-                       slot_to_row, cand_slot);
-  }
+#define MOE_SCATTER(HK, CAND)                                                                \
+  hipLaunchKernelGGL((scatter_kernel<HK, CAND>), grid, dim3(64 * kLayoutWaves), lds, s, ids,   \
+                     keep, p.T, p.E, p.k, nchunks, chunk_base, counts, offsets, row_token,     \
+                     slot_to_row, cand_slot)
+  if (cand_slot)
+    MOE_SCATTER(false, true);
+  else if (keep)
+    MOE_SCATTER(true, false);
+  else
+    MOE_SCATTER(false, false);
+#undef MOE_SCATTER
   return hipGetLastError();
 }
 

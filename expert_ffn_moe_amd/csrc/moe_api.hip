@@ -304,11 +304,8 @@ hipError_t run_capacity(const moe_problem& p, int32_t* ids, float* w, uint8_t* k
                         const RankScratch& r, hipStream_t s) {
   hipError_t err = hipSuccess;
   if (p.capacity <= 0) return err;
-  if ((err = launch_chunk_hist(p, ids, nullptr, r.chunk_hist, s)) != hipSuccess) return err;
-  if ((err = launch_scan(p, r.chunk_hist, r.chunk_base, r.cand_counts, s)) != hipSuccess)
-    return err;
-  if ((err = launch_scatter(p, ids, nullptr, r.chunk_base, r.cand_counts, r.cand_offsets,
-                            nullptr, nullptr, r.cand_slot, s)) != hipSuccess)
+  if ((err = launch_layout(p, ids, nullptr, r.chunk_hist, r.chunk_base, r.cand_counts,
+                           r.cand_offsets, nullptr, nullptr, r.cand_slot, s)) != hipSuccess)
     return err;
   return launch_capacity_select(p, r.cand_counts, r.cand_offsets, r.cand_slot, w, keep, s);
 }
@@ -336,11 +333,8 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
   err = launch_check_ids(p, ids, s);  // the ids may be the caller's
   if (err != hipSuccess) return err;
 #endif
-  err = launch_chunk_hist(p, ids, keep, r.chunk_hist, s);
-  if (err == hipSuccess) err = launch_scan(p, r.chunk_hist, r.chunk_base, counts, s);
-  if (err == hipSuccess)
-    err = launch_scatter(p, ids, keep, r.chunk_base, counts, offsets, row_token, slot_to_row,
-                         nullptr, s);
+  err = launch_layout(p, ids, keep, r.chunk_hist, r.chunk_base, counts, offsets, row_token,
+                      slot_to_row, nullptr, s);
   if (err == hipSuccess && xp) err = launch_gather(p, x, slot_to_row, xp, s);
   return err;
 }

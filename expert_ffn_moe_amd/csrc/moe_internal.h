@@ -65,19 +65,15 @@ hipError_t launch_router(const moe_problem& p, const void* x, const void* wr, in
                          uint8_t* keep, hipStream_t s);
 
 // ---- dispatch.hip
-// Per-chunk histogram of (kept) assignments per expert.
-hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                             int32_t* chunk_hist, hipStream_t s);
-// Column scan over chunks per expert -> chunk_base, counts.
-hipError_t launch_scan(const moe_problem& p, const int32_t* chunk_hist, int32_t* chunk_base,
-                       int32_t* counts, hipStream_t s);
-// Stable scatter: offsets = exclusive scan of counts (written out), then the row of each
-// kept slot.  If cand_slot != NULL the rows index the slot list cand_slot (capacity
-// candidates) instead of writing row_token / slot_to_row.
-hipError_t launch_scatter(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
-                          const int32_t* chunk_base, const int32_t* counts, int32_t* offsets,
-                          int32_t* row_token, int32_t* slot_to_row, int32_t* cand_slot,
-                          hipStream_t s);
+// The expert layout of the (kept) slots: counts, offsets = their exclusive scan (both written
+// out), then the row of each kept slot (stable: rows ascend in token index within an
+// expert).  If cand_slot != NULL the rows index the slot list cand_slot (capacity
+// candidates) instead of writing row_token / slot_to_row.  Three launches: the per-chunk
+// histogram, its column scan and the scatter (chunk_hist, chunk_base: [nchunks, E] scratch).
+hipError_t launch_layout(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
+                         int32_t* chunk_hist, int32_t* chunk_base, int32_t* counts,
+                         int32_t* offsets, int32_t* row_token, int32_t* slot_to_row,
+                         int32_t* cand_slot, hipStream_t s);
 // Capacity: per overflowing expert, radix-select the top-C keys and clear keep for the rest.
 hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
                                   const int32_t* cand_offsets, const int32_t* cand_slot,

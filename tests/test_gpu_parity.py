@@ -199,6 +199,12 @@ ROUTING = [
     Workload("all_to_one_cap_big", T=20000, H=64, E=8, k=2, I=64, capacity=5000, dtype="bf16",
              logits="all_to_one", seed=29),
     Workload("E1_k1", T=3, H=64, E=1, k=1, I=64, capacity=0, dtype="bf16", logits="normal", seed=28),
+    # more than 65536 slots: the layout's three-launch path (histogram, scan, scatter) at
+    # E <= 256, with and without a capacity (smaller problems take the one-launch path)
+    Workload("many_chunks", T=20000, H=64, E=64, k=4, I=64, capacity=0, dtype="bf16",
+             logits="normal+bias0.5", seed=30),
+    Workload("many_chunks_cap", T=18000, H=64, E=64, k=4, I=64, capacity=400, dtype="bf16",
+             logits="normal", seed=32),
 ]
 
 
@@ -217,6 +223,16 @@ def test_routing_and_dispatch_edge_cases(wl):
     N = lay["N"]
     xp = oracle.gather(host(x), lay["row_token"], N)
     assert np.array_equal(host(d["xp"])[:N], xp)
+    # the layer builds its layout from the selection's own histogram: the same layout
+    inp = synth.make_inputs(wl, DEV)
+    assert torch.equal(inp["logits"], logits)
+    pgu, pd = m.pack_weights(p, inp["w_gate"], inp["w_up"], inp["w_down"])
+    r = m.routing_buffers(p)
+    m.layer(p, inp["x"], inp["logits"], pgu, pd, routing=r)
+    torch.cuda.synchronize()
+    for n in ("topk_ids", "topk_w", "keep", "counts", "offsets", "slot_to_row"):
+        assert torch.equal(r[n], g[n]), n
+    assert torch.equal(r["row_token"][:N], g["row_token"][:N])
 
 
 def test_dispatch_without_keep_and_with_caller_routing():
