@@ -111,12 +111,12 @@ def roofline_of(stage, alg, sec, dtype):
                 frac=round(ach / PEAK_HBM_GBS, 4))
 
 
-def kernel_source_hash(csrc=None):
-    """Hash of the kernel sources with comments and blank lines removed (a comment edit
-    leaves the kernels, and so the recorded counters, valid)."""
+def kernel_source_hash(csrc=None, files=None):
+    """Hash of the kernel sources (all of them, or the named files) with comments and blank
+    lines removed (a comment edit leaves the kernels, and so the recorded counters, valid)."""
     h = hashlib.sha256()
     csrc = csrc or os.path.join(ROOT, "expert_ffn_moe_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files if files is not None else os.listdir(csrc)):
         text = open(os.path.join(csrc, f), encoding="utf-8").read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         lines = (re.sub(r"//.*$", "", ln).rstrip() for ln in text.splitlines())
@@ -126,12 +126,13 @@ def kernel_source_hash(csrc=None):
 
 def measured_traffic(workload, stage):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on the
-    current kernel sources (else None)."""
+    current sources of the stage's kernels (the record's kernel_files; all sources if it
+    names none), else None."""
     path = os.path.join(PROFILES, f"traffic_{stage}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sources") != kernel_source_hash():
+    if rec.get("kernel_sources") != kernel_source_hash(files=rec.get("kernel_files")):
         return None
     return rec.get("bytes_per_launch")
 

@@ -84,3 +84,14 @@ def test_kernel_source_hash_ignores_comments_only(tmp_path):
     assert bench.kernel_source_hash(str(tmp_path)) == h0
     src.write_text("__global__ void k(int* p) {\n  p[0] = 2;\n}\n")
     assert bench.kernel_source_hash(str(tmp_path)) != h0
+
+
+def test_kernel_source_hash_of_named_files_ignores_the_others(tmp_path):
+    (tmp_path / "a.hip").write_text("__global__ void a(int* p) { p[0] = 1; }\n")
+    (tmp_path / "b.hip").write_text("__global__ void b(int* p) { p[0] = 1; }\n")
+    h0 = bench.kernel_source_hash(str(tmp_path), ["a.hip"])
+    (tmp_path / "b.hip").write_text("__global__ void b(int* p) { p[0] = 2; }\n")
+    assert bench.kernel_source_hash(str(tmp_path), ["a.hip"]) == h0
+    assert bench.kernel_source_hash(str(tmp_path)) != bench.kernel_source_hash(str(tmp_path), ["a.hip"])
+    (tmp_path / "a.hip").write_text("__global__ void a(int* p) { p[0] = 3; }\n")
+    assert bench.kernel_source_hash(str(tmp_path), ["a.hip"]) != h0
