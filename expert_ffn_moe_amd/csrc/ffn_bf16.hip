@@ -323,8 +323,10 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
 // Scheduling: every block first turns `offsets` into per-expert M-tile starts (LDS).  The
 // M tiles are split into 8 contiguous ranges, one per XCD (workgroups are dispatched to
 // XCDs round-robin, so block b runs on XCD b % 8); the blocks of an XCD take its work
-// items in turn.  Items of one expert therefore run together on one XCD, and the weight
-// and activation bytes they share are served by that XCD's L2.
+// items in turn, expert by expert, and within an expert N group by N group with the M
+// tiles innermost (measured 2-3.5% faster than M-tile-major on the three prefill shapes).
+// Items of one expert therefore run together on one XCD, and the weight and activation
+// bytes they share are served by that XCD's L2.
 // ------------------------------------------------------------------------------------
 // GATHER (gate/up only): the activation rows are token rows x[row_token[r]] instead of
 // xp[r], so the dispatch row copy is folded into this kernel's activation loads.
@@ -374,15 +376,23 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
   const size_t panel = (size_t)nk16 * kOperandElems;
 
   for (int item = slot; item < items; item += nslots) {
-    const int mt = mt_lo + item / ntn;
-    const int nt = item - (item / ntn) * ntn;
-    // expert of tile mt: the largest e with s_start[e] <= mt
+    // The items of the range, expert by expert (its M tiles inside the range): N group
+    // major, M tile minor.  The expert's segment of items starts at ntn times its first
+    // tile's offset in the range, so the expert is that of tile mt_lo + item / ntn: the
+    // largest e with s_start[e] <= that tile.
     int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_start[mid] <= mt) lo = mid; else hi = mid;
+    {
+      const int q = mt_lo + item / ntn;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[mid] <= q) lo = mid; else hi = mid;
+      }
     }
     const int e = lo;
+    const int seg0 = max(s_start[e], mt_lo), nte = min(s_start[e + 1], mt_hi) - seg0;
+    const int local = item - ntn * (seg0 - mt_lo);
+    const int nt = local / nte;
+    const int mt = seg0 + (local - nt * nte);
     const int row0 = offsets[e] + (mt - s_start[e]) * kPrefillBM;
     TileArgs t;
     t.rows = min(kPrefillBM, offsets[e + 1] - row0);
