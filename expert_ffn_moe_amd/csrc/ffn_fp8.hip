@@ -314,14 +314,21 @@ void fp8_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
   const size_t spanel = (size_t)div_up(nks, 4) * 64;  // scale words per panel
 
   for (int item = slot; item < items; item += nslots) {
-    const int mt = mt_lo + item / ntn;
-    const int nt = item - (item / ntn) * ntn;
+    // expert by expert, N group major and M tile minor, as in the bf16 prefill kernel: the
+    // expert is that of tile mt_lo + item / ntn
     int lo = 0, hi = E;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_start[mid] <= mt) lo = mid; else hi = mid;
+    {
+      const int q = mt_lo + item / ntn;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_start[mid] <= q) lo = mid; else hi = mid;
+      }
     }
     const int e = lo;
+    const int seg0 = max(s_start[e], mt_lo), nte = min(s_start[e + 1], mt_hi) - seg0;
+    const int local = item - ntn * (seg0 - mt_lo);
+    const int nt = local / nte;
+    const int mt = seg0 + (local - nt * nte);
     const int row0 = offsets[e] + (mt - s_start[e]) * kBM;
     Tile8 t;
     t.rows = min(kBM, offsets[e + 1] - row0);
