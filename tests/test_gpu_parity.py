@@ -199,8 +199,8 @@ ROUTING = [
     Workload("all_to_one_cap_big", T=20000, H=64, E=8, k=2, I=64, capacity=5000, dtype="bf16",
              logits="all_to_one", seed=29),
     Workload("E1_k1", T=3, H=64, E=1, k=1, I=64, capacity=0, dtype="bf16", logits="normal", seed=28),
-    # more than 65536 slots: the layout's three-launch path (histogram, scan, scatter) at
-    # E <= 256, with and without a capacity (smaller problems take the one-launch path)
+    # layouts of more than 65536 slots over 300 chunks, with and without a capacity (the
+    # column scan then splits each expert's chunks over all 16 wavefronts of its block)
     Workload("many_chunks", T=20000, H=64, E=64, k=4, I=64, capacity=0, dtype="bf16",
              logits="normal+bias0.5", seed=30),
     Workload("many_chunks_cap", T=18000, H=64, E=64, k=4, I=64, capacity=400, dtype="bf16",
