@@ -592,14 +592,6 @@ hipError_t launch_wgrad_bf16(const void* AT, const void* BT, const int32_t* poff
 // Decode shape: few rows per expert on average.
 bool ffn_use_decode(const moe_problem& p) { return (int64_t)p.T * p.k <= (int64_t)24 * p.E; }
 
-// Many rows per expert on average (the matrix cores bound the GEMMs, not the weight stream):
-// the plain GEMMs take the 256 x 256 tile (grouped_bf16.hip), which moves fewer bytes per
-// flop; below that the 128-row tiles waste less on ragged experts.  Both accumulate in the
-// same order, so the choice does not change any bit.
-bool ffn_use_wide_tile(const moe_problem& p) {
-  return (int64_t)p.T * p.k >= (int64_t)kWideTileRows * p.E;
-}
-
 namespace {
 int cu_count() {
   static int n = 0;
@@ -653,10 +645,8 @@ hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32
 // ([e][n32][k16] blocks), bf16 out.  The backward pass's data-gradient GEMMs.
 hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
                             const int32_t* offsets, const void* packed_b, void* out, int K,
-                            int Nout, bool decode, bool wide, hipStream_t s) {
+                            int Nout, bool decode, hipStream_t s) {
   const int nf32 = Nout / 32;
-  if (wide && !decode && K % 64 == 0 && Nout % 64 == 0)
-    return launch_grouped_bf16(E, A, row_token, offsets, packed_b, out, K, Nout, s);
   if (decode) {
     if (row_token)
       hipLaunchKernelGGL((decode_kernel<false, true>), dim3(div_up(nf32 / 2, 4), E), dim3(256), 0,
@@ -686,8 +676,6 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
     hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
                        0, s, (const uint16_t*)a, nullptr, offsets, (const uint16_t*)packed_d,
                        (uint16_t*)yp, p.I, p.H, nullptr);
-  } else if (ffn_use_wide_tile(p)) {
-    return launch_grouped_bf16(p.E, a, nullptr, offsets, packed_d, yp, p.I, p.H, s);
   } else {
     hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()), dim3(kThreads),
                        0, s, (const uint16_t*)a, nullptr, offsets, p.E,

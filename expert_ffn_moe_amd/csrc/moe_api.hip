@@ -825,7 +825,7 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   if (c.used > ws_bytes) return MOE_ERR_WORKSPACE;  // (sized by the same carve)
   hipStream_t s = as_stream(stream);
   const moe_saved_routing& R = *saved;
-  const bool dec = ffn_use_decode(*p), wide = ffn_use_wide_tile(*p);
+  const bool dec = ffn_use_decode(*p);
   const int H = p->H, I = p->I, E = p->E;
   float* dw = grads->dtopk_w ? grads->dtopk_w : B.dw;
   hipError_t err = hipSuccess;
@@ -844,11 +844,9 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
   // data gradients: da = dyp W_down^T; g|u (saved, or recomputed); SwiGLU backward;
   // dxp = dgu [Wg|Wu]^T
   if (err == hipSuccess)
-    err = launch_gemm_bf16(E, B.dyp, nullptr, R.offsets, packed_bwd_down, B.da, H, I, dec, wide,
-                           s);
+    err = launch_gemm_bf16(E, B.dyp, nullptr, R.offsets, packed_bwd_down, B.da, H, I, dec, s);
   if (err == hipSuccess && !gu) {
-    err = launch_gemm_bf16(E, x, R.row_token, R.offsets, packed_gate_up, B.gu, H, 2 * I, dec,
-                           wide, s);
+    err = launch_gemm_bf16(E, x, R.row_token, R.offsets, packed_gate_up, B.gu, H, 2 * I, dec, s);
     gu = B.gu;
   }
   if (err == hipSuccess) err = launch_pad_offsets(R.offsets, E, 64, B.poff, s);
@@ -856,7 +854,7 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
     err = launch_swiglu_bwd(*p, gu, B.da, R.offsets, B.poff, B.npad, B.dgu, B.dguT, B.aT, s);
   if (err == hipSuccess)
     err = launch_gemm_bf16(E, B.dgu, nullptr, R.offsets, packed_bwd_gate_up, B.dxp, 2 * I, H,
-                           dec, wide, s);
+                           dec, s);
   // the router's path: dx_r = dlogits W_r (added in the sum below), dW_r = dlogits^T x
   const void* dxr = nullptr;
   if (w_router && err == hipSuccess) {
@@ -864,8 +862,8 @@ int moe_layer_backward(const moe_problem* p, const void* x, const float* logits,
     if (err == hipSuccess) err = launch_one_expert_offsets(B.roff, p->T, s);
     if (err == hipSuccess) err = launch_pack_plain(1, E, H, w_router, B.wr_packed, s);
     if (err == hipSuccess)
-      err = launch_gemm_bf16(1, B.dl16, nullptr, B.roff, B.wr_packed, B.dxr, E, H,
-                             p->T <= 24, false, s);
+      err = launch_gemm_bf16(1, B.dl16, nullptr, B.roff, B.wr_packed, B.dxr, E, H, p->T <= 24,
+                             s);
     if (err == hipSuccess) err = launch_pad_offsets(B.roff, 1, 64, B.rpoff, s);
     if (err == hipSuccess)
       err = launch_transpose_pad(B.dl16, nullptr, B.roff, B.rpoff, 1, E, B.tpad, false, B.dlT, s);

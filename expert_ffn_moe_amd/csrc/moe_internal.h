@@ -130,9 +130,6 @@ hipError_t launch_pack_plain(int E, int K, int N, const void* w, void* packed, h
 // The decode-shaped kernels (few rows per expert) or the prefill ones: decided from the
 // whole problem (a chunked layer decides once, so every chunk uses the same kernels).
 bool ffn_use_decode(const moe_problem& p);
-// Average rows per expert from which the plain GEMMs take the 256 x 256 tile.
-constexpr int kWideTileRows = 384;
-bool ffn_use_wide_tile(const moe_problem& p);
 // Gate/up over the layout's rows: row r reads xs[r] (xp), or xs[row_token[r]] (token rows
 // x) when row_token is not NULL.  gu, if not NULL, receives the pre-activations [rows, 2I]
 // exactly as launch_gemm_bf16 over the packed gate/up weights computes them.
@@ -143,16 +140,9 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
                             const void* packed_d, void* yp, bool decode, hipStream_t s);
 // Plain grouped GEMM out[r] = A[r or row_token[r]] B[e] with B packed like the down weights
 // (K % 64 == 0 for the prefill kernel, K % 32 for the decode one; Nout % 64 == 0).
-// wide: the 256 x 256 tile (grouped_bf16.hip) when K % 64 == 0 and Nout % 64 == 0.
 hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
                             const int32_t* offsets, const void* packed_b, void* out, int K,
-                            int Nout, bool decode, bool wide, hipStream_t s);
-// The plain grouped GEMM on 256 x 256 tiles (grouped_bf16.hip): out[r] = A[r or
-// row_token[r]] B[e], B packed like the down weights; K % 64 == 0, Nout % 64 == 0; the same
-// bits as launch_gemm_bf16's other kernels.
-hipError_t launch_grouped_bf16(int E, const void* A, const int32_t* row_token,
-                               const int32_t* offsets, const void* packed_b, void* out, int K,
-                               int Nout, hipStream_t s);
+                            int Nout, bool decode, hipStream_t s);
 // Weight gradients on the matrix cores: out[e][m][n] = sum_k AT[m][k] BT[n][k] over expert
 // e's rows [poff[e], poff[e + 1]) (a multiple of 64, zero-padded); Ncols % 64 == 0.  AT is
 // row-major [M][npad]; BT is [Ncols][npad] in the packed operand order of

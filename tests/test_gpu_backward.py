@@ -145,9 +145,9 @@ SMALL = [
     # wavefronts, skewed experts with odd stage counts along their rows
     Workload("bwd_multi_tile", T=1000, H=384, E=8, k=2, I=320, capacity=0, dtype="bf16",
              logits="normal+zipf1.2", seed=76),
-    # over 384 rows per expert: the data-gradient GEMMs (and the g|u recompute) on the
-    # 256 x 256 tile, ragged in rows and in columns (I = 192: a partial N tile)
-    Workload("bwd_wide_tile", T=1200, H=256, E=4, k=2, I=192, capacity=0, dtype="bf16",
+    # 600 rows per expert on average: the data-gradient GEMMs (and the g|u recompute) over
+    # several 128-row M tiles per expert, ragged in rows and in columns (I = 192)
+    Workload("bwd_many_tiles", T=1200, H=256, E=4, k=2, I=192, capacity=0, dtype="bf16",
              logits="normal", seed=77),
 ]
 

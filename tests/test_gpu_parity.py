@@ -158,9 +158,9 @@ SMALL = [
     Workload("f32_cap_ties", T=100, H=64, E=4, k=2, I=32, capacity=30, dtype="f32",
              logits="ties012", seed=17),
     synth.WORKLOADS["tiny_f32"],
-    # over 384 rows per expert: the down projection on the 256 x 256 tile, several M tiles
-    # per expert with ragged tails, a partial N tile (H = 320: 10 panels)
-    Workload("prefill_wide_tile", T=2000, H=320, E=4, k=2, I=192, capacity=0, dtype="bf16",
+    # 500 rows per expert on average: four or five 128-row M tiles per expert with ragged
+    # tails, a partial N group (H = 320: 10 panels)
+    Workload("prefill_many_tiles", T=2000, H=320, E=4, k=2, I=192, capacity=0, dtype="bf16",
              logits="normal+bias0.5", seed=19),
     # many experts on the prefill kernels (T*k > 24 E): expert lookup and XCD ranges over
     # 600 experts, most with a handful of rows, some empty
@@ -364,37 +364,3 @@ def test_full_size_workload(name):
     del g, inp
     torch.cuda.empty_cache()
 
-
-def test_down_tile_choice_changes_no_bit():
-    """The down projection takes the 256 x 256 kernel when the experts average 384 rows or
-    more and the 128-row kernel below that; both accumulate in the same order.  The same
-    rows and weights laid out once as 4 experts (2000 rows: the wide kernel) and once as 8
-    experts of which the last 4 are empty (the 128-row kernel) give the same bits."""
-    m = moe()
-    torch.manual_seed(71)
-    T, k, H, I = 1000, 2, 320, 192
-    p_wide = m.Problem(T=T, H=H, E=4, k=k, I=I)
-    p_narrow = m.Problem(T=T, H=H, E=8, k=k, I=I)
-    a = (torch.randn(T * k, I, device=DEV) * 0.5).to(torch.bfloat16)
-    wg = (torch.randn(8, H, I, device=DEV) * 0.05).to(torch.bfloat16)
-    wu = (torch.randn(8, H, I, device=DEV) * 0.05).to(torch.bfloat16)
-    wd = (torch.randn(8, I, H, device=DEV) * 0.05).to(torch.bfloat16)
-    off_wide = torch.tensor([0, 300, 900, 1400, 2000], dtype=torch.int32, device=DEV)
-    off_narrow = torch.tensor([0, 300, 900, 1400, 2000, 2000, 2000, 2000, 2000],
-                              dtype=torch.int32, device=DEV)
-    _, pd_wide = m.pack_weights(p_wide, wg[:4].contiguous(), wu[:4].contiguous(),
-                                wd[:4].contiguous())
-    _, pd_narrow = m.pack_weights(p_narrow, wg, wu, wd)
-    y_wide = m.expert_down(p_wide, a, off_wide, pd_wide)
-    y_narrow = m.expert_down(p_narrow, a, off_narrow, pd_narrow)
-    torch.cuda.synchronize()
-    assert torch.equal(y_wide, y_narrow)
-    # and against fp64 products of the same bf16 operands on a few rows of every expert
-    ref = np.zeros((T * k, H))
-    a64, wd64 = host(a.float()).astype(np.float64), host(wd.float()).astype(np.float64)
-    o = host(off_wide)
-    for e in range(4):
-        rows = np.array([o[e], (o[e] + o[e + 1]) // 2, o[e + 1] - 1])
-        ref[rows] = a64[rows] @ wd64[e]
-        got = host(y_wide[rows].float()).astype(np.float64)
-        assert np.abs(got - ref[rows]).max() <= 2e-2 * np.abs(ref[rows]).max()
