@@ -139,7 +139,7 @@ __device__ __forceinline__ void kstage(f32x16_t (&acc)[NM][2], i32x8 (&bring)[2]
   __syncthreads();
 }
 
-// One work item: NM 32-row blocks (NM = 4, or 2 for a tile with at most 64 rows) x this
+// One work item: NM 32-row blocks (NM = 4, or 2 / 1 for a tile with at most 64 / 32 rows) x this
 // wavefront's two operand columns.
 template <bool GATE_UP, bool GATHER, int NM>
 __device__ __forceinline__ void tile8(const Tile8& t, u32x4 (*lds)[1024], uint32_t (*lds_s)[kThreads],
@@ -369,8 +369,10 @@ void fp8_kernel(const uint8_t* __restrict__ A, const uint8_t* __restrict__ As,
     }
     if (t.rows > 64)  // block-uniform
       tile8<GATE_UP, GATHER, 4>(t, lds_a, lds_s, tid);
-    else
+    else if (t.rows > 32)
       tile8<GATE_UP, GATHER, 2>(t, lds_a, lds_s, tid);
+    else
+      tile8<GATE_UP, GATHER, 1>(t, lds_a, lds_s, tid);
   }
 }
 
