@@ -99,8 +99,10 @@ __global__ __launch_bounds__(64 * kLayoutWaves) void chunk_hist_kernel(const int
 __global__ __launch_bounds__(1024) void scan_cols_kernel(const int32_t* __restrict__ chunk_hist,
                                                          int E, int nchunks,
                                                          int32_t* __restrict__ chunk_base,
-                                                         int32_t* __restrict__ counts) {
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ zero_claims) {
   __shared__ int part[16][64];
+  if (zero_claims && blockIdx.x == 0 && threadIdx.x < kClaimInts) zero_claims[threadIdx.x] = 0;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 64 + lane;
   const int per = div_up(nchunks, 16);
@@ -361,12 +363,12 @@ static hipError_t launch_chunk_hist(const moe_problem& p, const int32_t* ids,
 hipError_t launch_layout(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
                          int32_t* chunk_hist, int32_t* chunk_base, int32_t* counts,
                          int32_t* offsets, int32_t* row_token, int32_t* slot_to_row,
-                         int32_t* cand_slot, hipStream_t s) {
+                         int32_t* cand_slot, hipStream_t s, int32_t* zero_claims) {
   const int nchunks = div_up(p.T, kChunk);
   hipError_t err = launch_chunk_hist(p, ids, keep, chunk_hist, s);
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(scan_cols_kernel, dim3(div_up(p.E, 64)), dim3(1024), 0, s, chunk_hist, p.E,
-                     nchunks, chunk_base, counts);
+                     nchunks, chunk_base, counts, zero_claims);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   dim3 grid(div_up(nchunks, kLayoutWaves));
   const size_t lds = bitmap_lds(p);

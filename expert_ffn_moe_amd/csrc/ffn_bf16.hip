@@ -333,7 +333,12 @@ __device__ __forceinline__ void prefill_tile(const TileArgs& t, u32x4 (*lds)[102
 // items in turn, expert by expert, and within an expert N group by N group with the M
 // tiles innermost (measured 2-3.5% faster than M-tile-major on the three prefill shapes).
 // Items of one expert therefore run together on one XCD, and the weight and activation
-// bytes they share are served by that XCD's L2.
+// bytes they share are served by that XCD's L2.  Without `claim` the blocks of an XCD take
+// its items round-robin; with it (8 counters, zero at launch) a block's first item is its
+// slot and each further item is claimed from its XCD's counter when the block starts the
+// item before (the atomic's latency hides behind that item), so blocks that drew short
+// tiles take more items: with only a few items per block (the smaller prefill shapes) the
+// static split ends with some blocks idle while others still run.
 // ------------------------------------------------------------------------------------
 // GATHER (gate/up only): the activation rows are token rows x[row_token[r]] instead of
 // xp[r], so the dispatch row copy is folded into this kernel's activation loads.
@@ -344,10 +349,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
                     const int32_t* __restrict__ offsets, int E,
                     const uint16_t* __restrict__ Bp, uint16_t* __restrict__ out, int K, int Nout,
-                    uint16_t* __restrict__ gu) {
+                    uint16_t* __restrict__ gu, int* __restrict__ claim) {
   __shared__ u32x4 lds_a[2][1024];  // two activation stages (see a_slot)
   __shared__ int s_start[kMaxExperts + 1];
   __shared__ int s_wsum[kWaves];
+  __shared__ int s_claim[2];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -382,7 +388,11 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
   const int items = (mt_hi - mt_lo) * ntn;
   const size_t panel = (size_t)nk16 * kOperandElems;
 
-  for (int item = slot; item < items; item += nslots) {
+  int cpar = 0;
+  for (int item = slot; item < items;) {
+    int claimed = 0;
+    if (claim != nullptr && tid == 0)
+      claimed = __hip_atomic_fetch_add(claim + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // The items of the range, expert by expert (its M tiles inside the range): N group
     // major, M tile minor.  The expert's segment of items starts at ntn times its first
     // tile's offset in the range, so the expert is that of tile mt_lo + item / ntn: the
@@ -438,6 +448,15 @@ void prefill_kernel(const uint16_t* __restrict__ A, const int32_t* __restrict__ 
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) t.fbase[kk] = a_slot(lane_v & 31, 2 * kk + (lane_v >> 5));
     prefill_tile<GATE_UP ? kModeGateUp : kModeDown, GATHER, SAVE_GU>(t, lds_a);
+    if (claim != nullptr) {  // block-uniform
+      // two LDS slots: the slot written here was last read before the previous barrier
+      if (tid == 0) s_claim[cpar] = claimed;
+      __syncthreads();
+      item = nslots + s_claim[cpar];
+      cpar ^= 1;
+    } else {
+      item += nslots;
+    }
   }
 }
 
@@ -619,7 +638,7 @@ namespace {
 template <bool GATHER, bool SAVE_GU>
 void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
                   const int32_t* offsets, const void* packed_gu, void* a, void* gu, bool decode,
-                  hipStream_t s) {
+                  hipStream_t s, int* claim) {
   if (decode) {
     const int nf32 = p.I / 32;
     hipLaunchKernelGGL((decode_kernel<true, GATHER, SAVE_GU>), dim3(div_up(nf32, 4), p.E),
@@ -628,22 +647,22 @@ void gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token
   } else {
     hipLaunchKernelGGL((prefill_kernel<true, GATHER, SAVE_GU>), dim3(persistent_grid()),
                        dim3(kThreads), 0, s, (const uint16_t*)xs, row_token, offsets, p.E,
-                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I, (uint16_t*)gu);
+                       (const uint16_t*)packed_gu, (uint16_t*)a, p.H, p.I, (uint16_t*)gu, claim);
   }
 }
 }  // namespace
 
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
                                const int32_t* offsets, const void* packed_gu, void* a, void* gu,
-                               bool decode, hipStream_t s) {
+                               bool decode, hipStream_t s, int* claim) {
   if (row_token && gu)
-    gate_up_bf16<true, true>(p, xs, row_token, offsets, packed_gu, a, gu, decode, s);
+    gate_up_bf16<true, true>(p, xs, row_token, offsets, packed_gu, a, gu, decode, s, claim);
   else if (row_token)
-    gate_up_bf16<true, false>(p, xs, row_token, offsets, packed_gu, a, nullptr, decode, s);
+    gate_up_bf16<true, false>(p, xs, row_token, offsets, packed_gu, a, nullptr, decode, s, claim);
   else if (gu)
-    gate_up_bf16<false, true>(p, xs, nullptr, offsets, packed_gu, a, gu, decode, s);
+    gate_up_bf16<false, true>(p, xs, nullptr, offsets, packed_gu, a, gu, decode, s, claim);
   else
-    gate_up_bf16<false, false>(p, xs, nullptr, offsets, packed_gu, a, nullptr, decode, s);
+    gate_up_bf16<false, false>(p, xs, nullptr, offsets, packed_gu, a, nullptr, decode, s, claim);
   return hipGetLastError();
 }
 
@@ -667,17 +686,18 @@ hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
     if (row_token)
       hipLaunchKernelGGL((prefill_kernel<false, true>), dim3(persistent_grid()), dim3(kThreads),
                          0, s, (const uint16_t*)A, row_token, offsets, E,
-                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr);
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr, nullptr);
     else
       hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()),
                          dim3(kThreads), 0, s, (const uint16_t*)A, nullptr, offsets, E,
-                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr);
+                         (const uint16_t*)packed_b, (uint16_t*)out, K, Nout, nullptr, nullptr);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, bool decode, hipStream_t s) {
+                            const void* packed_d, void* yp, bool decode, hipStream_t s,
+                            int* claim) {
   if (decode) {
     const int nf32 = p.H / 32;
     hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
@@ -686,7 +706,7 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
   } else {
     hipLaunchKernelGGL((prefill_kernel<false, false>), dim3(persistent_grid()), dim3(kThreads),
                        0, s, (const uint16_t*)a, nullptr, offsets, p.E,
-                       (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H, nullptr);
+                       (const uint16_t*)packed_d, (uint16_t*)yp, p.I, p.H, nullptr, claim);
   }
   return hipGetLastError();
 }

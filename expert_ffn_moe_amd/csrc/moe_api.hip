@@ -134,6 +134,7 @@ ChunkScratch carve_chunked(Carve& c, const moe_problem& p, int chunk_tokens, int
 
 struct LayerScratch {
   int32_t *ids, *counts, *offsets, *row_token, *slot_to_row;
+  int32_t* claims;  // the prefill GEMMs' work-item counters (zeroed by the layout)
   float* w;
   uint8_t* keep;
   void* yp;
@@ -151,6 +152,7 @@ LayerScratch carve_layer(Carve& c, const moe_problem& p) {
   L.offsets = c.take<int32_t>((size_t)p.E + 1);
   L.row_token = c.take<int32_t>(tk);
   L.slot_to_row = c.take<int32_t>(tk);
+  L.claims = c.take<int32_t>(kClaimInts);
   L.yp = c.take<char>(tk * p.H * eb);
   L.rank = carve_rank(c, p, p.capacity > 0);
   L.ffn = carve_ffn(c, p);
@@ -327,14 +329,14 @@ bool groups_ok(const moe_problem& p, int n_group, int topk_group) {
 hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
                         const uint8_t* keep, int32_t* counts, int32_t* offsets,
                         int32_t* row_token, int32_t* slot_to_row, void* xp,
-                        const RankScratch& r, hipStream_t s) {
+                        const RankScratch& r, hipStream_t s, int32_t* zero_claims = nullptr) {
   hipError_t err = hipSuccess;
 #ifdef MOE_DEBUG_CHECKS
   err = launch_check_ids(p, ids, s);  // the ids may be the caller's
   if (err != hipSuccess) return err;
 #endif
   err = launch_layout(p, ids, keep, r.chunk_hist, r.chunk_base, counts, offsets, row_token,
-                      slot_to_row, nullptr, s);
+                      slot_to_row, nullptr, s, zero_claims);
   if (err == hipSuccess && xp) err = launch_gather(p, x, slot_to_row, xp, s);
   return err;
 }
@@ -345,7 +347,7 @@ hipError_t run_dispatch(const moe_problem& p, const void* x, const int32_t* ids,
 // gu (bf16 only): also store the pre-activations g|u.
 hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_token,
                        const int32_t* offsets, const void* pgu, void* a, const FfnScratch& f,
-                       bool decode, hipStream_t s, void* gu = nullptr) {
+                       bool decode, hipStream_t s, void* gu = nullptr, int* claim = nullptr) {
   if (is_fp8(p)) {
     const size_t tk = (size_t)p.T * p.k;
     const size_t rows = row_token ? (size_t)p.T : tk;
@@ -363,11 +365,11 @@ hipError_t run_gate_up(const moe_problem& p, const void* xs, const int32_t* row_
     return launch_gate_up_f32(p, (const float*)xs, row_token, offsets, (const float*)pgu,
                               (const float*)pgu + n, (float*)a, s);
   }
-  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, gu, decode, s);
+  return launch_gate_up_bf16(p, xs, row_token, offsets, pgu, a, gu, decode, s, claim);
 }
 
 hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
-                    const void* pd, void* yp, bool decode, hipStream_t s) {
+                    const void* pd, void* yp, bool decode, hipStream_t s, int* claim = nullptr) {
   if (is_fp8(p)) {
     const size_t tk = (size_t)p.T * p.k;
     return launch_down_fp8(p, static_cast<const uint8_t*>(a),
@@ -375,7 +377,7 @@ hipError_t run_down(const moe_problem& p, const void* a, const int32_t* offsets,
   }
   if (p.act_dtype == MOE_F32)
     return launch_down_f32(p, (const float*)a, offsets, (const float*)pd, (float*)yp, s);
-  return launch_down_bf16(p, a, offsets, pd, yp, decode, s);
+  return launch_down_bf16(p, a, offsets, pd, yp, decode, s, claim);
 }
 
 // ---- the no-allocation layer (moe_layer_static): moe_layer's workspace in a file-scope
@@ -729,12 +731,13 @@ int moe_layer(const moe_problem* p, const void* x, const float* logits,
   // dispatch builds the layout only: gate/up reads the token rows through row_token
   if (err == hipSuccess)
     err = run_dispatch(*p, x, topk_ids, p->capacity > 0 ? keep : nullptr, counts, offsets,
-                       row_token, slot_to_row, nullptr, L.rank, s);
+                       row_token, slot_to_row, nullptr, L.rank, s, L.claims);
   if (err == hipSuccess)
     err = run_gate_up(*p, x, row_token, offsets, packed_gate_up, L.ffn.a, L.ffn,
-                      ffn_use_decode(*p), s);
+                      ffn_use_decode(*p), s, nullptr, L.claims);
   if (err == hipSuccess)
-    err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, ffn_use_decode(*p), s);
+    err = run_down(*p, L.ffn.a, offsets, packed_down, L.yp, ffn_use_decode(*p), s,
+                   L.claims + kClaimInts / 2);
   if (err == hipSuccess) err = launch_combine(*p, L.yp, topk_w, slot_to_row, nullptr, y, s);
   return status_of(err);
 }

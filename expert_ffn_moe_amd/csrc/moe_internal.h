@@ -70,10 +70,12 @@ hipError_t launch_router(const moe_problem& p, const void* x, const void* wr, in
 // expert).  If cand_slot != NULL the rows index the slot list cand_slot (capacity
 // candidates) instead of writing row_token / slot_to_row.  Three launches: the per-chunk
 // histogram, its column scan and the scatter (chunk_hist, chunk_base: [nchunks, E] scratch).
+// zero_claims, if not NULL, receives kClaimInts zeros (the layer's GEMM work counters) from
+// the column scan.
 hipError_t launch_layout(const moe_problem& p, const int32_t* ids, const uint8_t* keep,
                          int32_t* chunk_hist, int32_t* chunk_base, int32_t* counts,
                          int32_t* offsets, int32_t* row_token, int32_t* slot_to_row,
-                         int32_t* cand_slot, hipStream_t s);
+                         int32_t* cand_slot, hipStream_t s, int32_t* zero_claims = nullptr);
 // Capacity: per overflowing expert, radix-select the top-C keys and clear keep for the rest.
 hipError_t launch_capacity_select(const moe_problem& p, const int32_t* cand_counts,
                                   const int32_t* cand_offsets, const int32_t* cand_slot,
@@ -133,11 +135,16 @@ bool ffn_use_decode(const moe_problem& p);
 // Gate/up over the layout's rows: row r reads xs[r] (xp), or xs[row_token[r]] (token rows
 // x) when row_token is not NULL.  gu, if not NULL, receives the pre-activations [rows, 2I]
 // exactly as launch_gemm_bf16 over the packed gate/up weights computes them.
+// claim, if not NULL: 8 work-item counters of the prefill kernel (one per XCD), zero at
+// launch; the blocks then take items dynamically instead of round-robin.
 hipError_t launch_gate_up_bf16(const moe_problem& p, const void* xs, const int32_t* row_token,
                                const int32_t* offsets, const void* packed_gu, void* a, void* gu,
-                               bool decode, hipStream_t s);
+                               bool decode, hipStream_t s, int* claim = nullptr);
 hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* offsets,
-                            const void* packed_d, void* yp, bool decode, hipStream_t s);
+                            const void* packed_d, void* yp, bool decode, hipStream_t s,
+                            int* claim = nullptr);
+// The work-item counters of one layer call: gate/up's 8, then down's 8.
+constexpr int kClaimInts = 16;
 // Plain grouped GEMM out[r] = A[r or row_token[r]] B[e] with B packed like the down weights
 // (K % 64 == 0 for the prefill kernel, K % 32 for the decode one; Nout % 64 == 0).
 hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
