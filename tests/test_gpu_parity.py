@@ -205,6 +205,12 @@ ROUTING = [
              logits="normal+bias0.5", seed=30),
     Workload("many_chunks_cap", T=18000, H=64, E=64, k=4, I=64, capacity=400, dtype="bf16",
              logits="normal", seed=32),
+    # 256 chunks with the last one ragged, and 250 chunks with a capacity (its candidate
+    # list too): chunk counts that split unevenly over the column scan's 16 wavefronts
+    Workload("fused_scan_limit", T=16383, H=64, E=64, k=4, I=64, capacity=0, dtype="bf16",
+             logits="normal", seed=33),
+    Workload("fused_scan_cap", T=16000, H=64, E=64, k=4, I=64, capacity=300, dtype="bf16",
+             logits="normal+bias0.5", seed=34),
 ]
 
 
