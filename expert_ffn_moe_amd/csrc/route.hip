@@ -263,6 +263,7 @@ hipError_t launch_select(const moe_problem& p, const float* logits, int S, int n
 // ---------------------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_r __attribute__((ext_vector_type(4)));
 
 constexpr int kRouterMaxE = 256;
 
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(64 * W) void router_gemm_kernel(const uint16_t* __r
   constexpr int E = 16 * NT;
   constexpr int kPieces = E * 8;                        // 16-byte pieces per chunk
   constexpr int kPer = (kPieces + 64 * W - 1) / (64 * W);  // per thread
-  __shared__ uint4 lds[2 * E * 8];
+  __shared__ u32x4_r lds[2 * E * 8];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int row0 = blockIdx.x * 16 * W;
@@ -288,19 +289,20 @@ __global__ __launch_bounds__(64 * W) void router_gemm_kernel(const uint16_t* __r
   f32x4_t acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = f32x4_t{};
-  uint4 pre[kPer];
+  // (vector types throughout: with the struct uint4, pre[] was kept in scratch memory)
+  u32x4_r pre[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int q = tid + 64 * W * j;
-    if (q < kPieces) pre[j] = *(const uint4*)(wp + (size_t)(q >> 3) * H + 8 * (q & 7));
+    if (q < kPieces) pre[j] = *(const u32x4_r*)(wp + (size_t)(q >> 3) * H + 8 * (q & 7));
   }
   // x chunks c, c + 1, c + 2 in registers (HBM latency spans a few chunks of MFMAs)
-  uint4 xa[3][2];
+  u32x4_r xa[3][2];
 #pragma unroll
   for (int d = 0; d < 3; ++d) {
     const int cd = min(d, cps - 1);
-    xa[d][0] = *(const uint4*)(ap + 64 * cd);
-    xa[d][1] = *(const uint4*)(ap + 64 * cd + 32);
+    xa[d][0] = *(const u32x4_r*)(ap + 64 * cd);
+    xa[d][1] = *(const u32x4_r*)(ap + 64 * cd + 32);
   }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -314,23 +316,24 @@ __global__ __launch_bounds__(64 * W) void router_gemm_kernel(const uint16_t* __r
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = tid + 64 * W * j;
-      if (q < kPieces) pre[j] = *(const uint4*)(wp + (size_t)(q >> 3) * H + 64 * cn + 8 * (q & 7));
+      if (q < kPieces)
+        pre[j] = *(const u32x4_r*)(wp + (size_t)(q >> 3) * H + 64 * cn + 8 * (q & 7));
     }
     const int c3 = min(c + 3, cps - 1);
-    const uint4 n0 = *(const uint4*)(ap + 64 * c3);
-    const uint4 n1 = *(const uint4*)(ap + 64 * c3 + 32);
-    const uint4* b = lds + buf * (E * 8);
+    const u32x4_r n0 = *(const u32x4_r*)(ap + 64 * c3);
+    const u32x4_r n1 = *(const u32x4_r*)(ap + 64 * c3 + 32);
+    const u32x4_r* b = lds + buf * (E * 8);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xa[0][ks]);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint4 bv = b[wr_slot(16 * t + (lane & 15), 4 * ks + (lane >> 4))];
+        const u32x4_r bv = b[wr_slot(16 * t + (lane & 15), 4 * ks + (lane >> 4))];
         acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, bv),
                                                           acc[t], 0, 0, 0);
       }
     }
-    uint4* nb = lds + (buf ^ 1) * (E * 8);
+    u32x4_r* nb = lds + (buf ^ 1) * (E * 8);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int q = tid + 64 * W * j;
