@@ -522,8 +522,12 @@ void wgrad_kernel(const uint16_t* __restrict__ AT, const uint16_t* __restrict__ 
 
 // ------------------------------------------------------------------------------------
 // Decode (weight streaming).  One wavefront per panel of one expert:
-//   GATE_UP: 32 columns of `a` (gate + up operand columns); DOWN: 64 columns of yp.
-// Each k-step of 32 issues 4 B operand loads (16 columns each) and one A load.
+//   GATE_UP: 32 columns of `a` (gate + up operand columns): each k-step of 32 issues 4 B
+//            operand loads (16 columns each) and one A load;
+//   DOWN   : 32 columns of yp, two k-steps per iteration (the same 4 B loads in flight).
+// The wavefronts hold few registers, so 32 of them share a CU; 32 columns each make the
+// DSV3-shaped down projection 224 wavefronts per CU (7 full rounds; with 64 columns it was
+// 3.5, the last round half empty).
 // ------------------------------------------------------------------------------------
 template <bool GATE_UP, bool GATHER, bool SAVE_GU = false>
 __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict__ A,
@@ -540,12 +544,12 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = blockIdx.x * 4 + wave;
   const int nf32 = Nout / 32;
-  const int ngroups = GATE_UP ? nf32 : nf32 / 2;
+  const int ngroups = nf32;
   if (g >= ngroups) return;  // no barriers in this kernel
   const int nk16 = K / 16;
   const uint16_t* base = GATE_UP
                              ? Bp + (size_t)(e * nf32 + g) * 2 * nk16 * kOperandElems
-                             : Bp + (size_t)(e * nf32 + 2 * g) * nk16 * kOperandElems;
+                             : Bp + (size_t)(e * nf32 + g) * nk16 * kOperandElems;
   const uint16_t* pb0 = base;
   const uint16_t* pb1 = base + (size_t)nk16 * kOperandElems;
   // 16x16x32 B operand from the 32x32x16 packed blocks: lane l takes column l%16 (+16 for
@@ -561,20 +565,51 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
     const int ar = row_beg + min(m0 + (lane & 15), cnt - 1);
     const size_t src_row = GATHER ? (size_t)row_token[ar] : (size_t)ar;
     const uint16_t* ap = A + src_row * K + 8 * (lane >> 4);
-    for (int ks = 0; ks < nks; ++ks) {
-      const uint4 av = *(const uint4*)(ap + ks * 32);
-      const size_t o = (size_t)(2 * ks + ksub) * kOperandElems + lofs;
-      // weights are read once per launch: non-temporal loads (measured 5-7% faster on
-      // 7168 x 2048 experts than cached loads)
-      const u32x4 v0 = __builtin_nontemporal_load((const u32x4*)(pb0 + o));
-      const u32x4 v1 = __builtin_nontemporal_load((const u32x4*)(pb0 + o + 16 * 8));
-      const u32x4 v2 = __builtin_nontemporal_load((const u32x4*)(pb1 + o));
-      const u32x4 v3 = __builtin_nontemporal_load((const u32x4*)(pb1 + o + 16 * 8));
-      const bf16x8_t a = as_bf16x8(av);
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v0), acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v1), acc[1], 0, 0, 0);
-      acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v2), acc[2], 0, 0, 0);
-      acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v3), acc[3], 0, 0, 0);
+    // weights are read once per launch: non-temporal loads (measured 5-7% faster on
+    // 7168 x 2048 experts than cached loads)
+    if constexpr (GATE_UP) {
+      for (int ks = 0; ks < nks; ++ks) {
+        const uint4 av = *(const uint4*)(ap + ks * 32);
+        const size_t o = (size_t)(2 * ks + ksub) * kOperandElems + lofs;
+        const u32x4 v0 = __builtin_nontemporal_load((const u32x4*)(pb0 + o));
+        const u32x4 v1 = __builtin_nontemporal_load((const u32x4*)(pb0 + o + 16 * 8));
+        const u32x4 v2 = __builtin_nontemporal_load((const u32x4*)(pb1 + o));
+        const u32x4 v3 = __builtin_nontemporal_load((const u32x4*)(pb1 + o + 16 * 8));
+        const bf16x8_t a = as_bf16x8(av);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v0), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v1), acc[1], 0, 0, 0);
+        acc[2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v2), acc[2], 0, 0, 0);
+        acc[3] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, as_bf16x8(v3), acc[3], 0, 0, 0);
+      }
+    } else {
+      // k-steps in pairs (their loads issued together), an odd last one alone, into the
+      // accumulators of the panel's two 16-column halves in k order
+      int ks = 0;
+      for (; ks + 1 < nks; ks += 2) {
+        const uint4 av0 = *(const uint4*)(ap + ks * 32);
+        const uint4 av1 = *(const uint4*)(ap + ks * 32 + 32);
+        const size_t o0 = (size_t)(2 * ks + ksub) * kOperandElems + lofs;
+        const size_t o1 = o0 + 2 * kOperandElems;
+        const u32x4 v0 = __builtin_nontemporal_load((const u32x4*)(pb0 + o0));
+        const u32x4 v1 = __builtin_nontemporal_load((const u32x4*)(pb0 + o0 + 16 * 8));
+        const u32x4 w0 = __builtin_nontemporal_load((const u32x4*)(pb0 + o1));
+        const u32x4 w1 = __builtin_nontemporal_load((const u32x4*)(pb0 + o1 + 16 * 8));
+        __builtin_amdgcn_sched_barrier(0);  // all six loads in flight before the first MFMA
+        const bf16x8_t a0 = as_bf16x8(av0), a1 = as_bf16x8(av1);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v0), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v1), acc[1], 0, 0, 0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(w0), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, as_bf16x8(w1), acc[1], 0, 0, 0);
+      }
+      if (ks < nks) {
+        const uint4 av0 = *(const uint4*)(ap + ks * 32);
+        const size_t o0 = (size_t)(2 * ks + ksub) * kOperandElems + lofs;
+        const u32x4 v0 = __builtin_nontemporal_load((const u32x4*)(pb0 + o0));
+        const u32x4 v1 = __builtin_nontemporal_load((const u32x4*)(pb0 + o0 + 16 * 8));
+        const bf16x8_t a0 = as_bf16x8(av0);
+        acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v0), acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, as_bf16x8(v1), acc[1], 0, 0, 0);
+      }
     }
     // 16x16 accumulator layout: element i of lane l is row 4*(l/16) + i, column l%16.
 #pragma unroll
@@ -594,11 +629,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const uint16_t* __restrict_
           o2[48] = to_bf16(acc[3][i]);
         }
       } else {
-        const int c = g * 64 + (lane & 15);
+        const int c = g * 32 + (lane & 15);
         o[c] = to_bf16(acc[0][i]);
         o[c + 16] = to_bf16(acc[1][i]);
-        o[c + 32] = to_bf16(acc[2][i]);
-        o[c + 48] = to_bf16(acc[3][i]);
       }
     }
   }
@@ -675,11 +708,11 @@ hipError_t launch_gemm_bf16(int E, const void* A, const int32_t* row_token,
   const int nf32 = Nout / 32;
   if (decode) {
     if (row_token)
-      hipLaunchKernelGGL((decode_kernel<false, true>), dim3(div_up(nf32 / 2, 4), E), dim3(256), 0,
+      hipLaunchKernelGGL((decode_kernel<false, true>), dim3(div_up(nf32, 4), E), dim3(256), 0,
                          s, (const uint16_t*)A, row_token, offsets, (const uint16_t*)packed_b,
                          (uint16_t*)out, K, Nout, nullptr);
     else
-      hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), E), dim3(256),
+      hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32, 4), E), dim3(256),
                          0, s, (const uint16_t*)A, nullptr, offsets, (const uint16_t*)packed_b,
                          (uint16_t*)out, K, Nout, nullptr);
   } else {
@@ -700,7 +733,7 @@ hipError_t launch_down_bf16(const moe_problem& p, const void* a, const int32_t* 
                             int* claim) {
   if (decode) {
     const int nf32 = p.H / 32;
-    hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32 / 2, 4), p.E), dim3(256),
+    hipLaunchKernelGGL((decode_kernel<false, false>), dim3(div_up(nf32, 4), p.E), dim3(256),
                        0, s, (const uint16_t*)a, nullptr, offsets, (const uint16_t*)packed_d,
                        (uint16_t*)yp, p.I, p.H, nullptr);
   } else {
