@@ -287,6 +287,35 @@ def test_layer_matches_staged_calls_and_is_deterministic():
         assert torch.equal(g2[n][:N], g[n][:N]), n
 
 
+def test_layer_with_a_dirty_workspace():
+    """moe_layer keeps no state in its workspace between calls: whatever the workspace holds
+    beforehand (its prefill GEMMs' work-item counters included, which the layer zeroes
+    itself), the output equals the staged calls' bit for bit.  A prefill-shaped problem
+    (4,000 rows per expert: 256 M tiles and 512 items per GEMM, two per block) so that the
+    blocks take items from the counters."""
+    m = moe()
+    wl = Workload("claims", T=16000, H=1024, E=8, k=2, I=512, capacity=0, dtype="bf16",
+                  logits="normal", seed=41)
+    say(f"case layer with a dirty workspace: {wl.name}")
+    p = problem_of(wl)
+    inp = synth.make_inputs(wl, DEV)
+    g = gpu_staged(p, inp)
+    ws = m.workspace(p, m.OP_LAYER, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    for fill in ("ones", "random", "random", "zeros"):
+        if fill == "ones":
+            ws.fill_(0xFF)
+        elif fill == "zeros":
+            ws.zero_()
+        else:
+            ws.copy_(torch.randint(0, 256, ws.shape, generator=gen, device=DEV,
+                                   dtype=torch.int32).to(torch.uint8))
+        y = m.layer(p, inp["x"], inp["logits"], g["pgu"], g["pd"], ws=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y, g["y"]), fill
+
+
 def test_expert_ffn_equals_gate_up_then_down():
     m = moe()
     wl = SMALL[0]
