@@ -49,7 +49,6 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
     const int v = tid + 256 * q;
     if (v < nvec) unpack8(dy[(size_t)t * nvec + v], f[q]);
   }
-#pragma unroll 4
   for (int j = 0; j < k; ++j) {
     const int r = s2r[(size_t)t * k + j];  // block-uniform
     const float wj = w[(size_t)t * k + j];
